@@ -1,0 +1,133 @@
+"""Part A of the oracle: plain attention in float64 -- test infrastructure only.
+
+This is the "exact result" every mode is compared with.  All three modes compute
+the same function in exact arithmetic, because softmax is unchanged by a
+per-row shift (paper-graph-ui summary of arXiv 2510.04212, section 3.4.5,
+"Mathematical equivalence in exact arithmetic").
+
+Forward (section 3.4.4, the three-line definition of P-bar, O-bar and O):
+    S = scale * Q K^T, causal entries (key index > query index) set to -inf
+    P = softmax of each row of S
+    O = P V,  LSE = log sum_t exp(S_t)
+Backward (section 3.4.2 "Failure is linked to the computation of delta" and
+section 3.4.3 "Derivation of the gradient error"):
+    dV = P^T dO,  dP = dO V^T,  delta = rowsum(dO o O)
+    dS = P o (dP - delta),  dQ = scale * dS K,  dK = scale * dS^T Q
+The pages give dQ only; dK and dV are the standard gradients of the same
+product (the plainest reading).
+
+Inputs are numpy arrays shaped [..., N, d] holding the values the kernel sees
+(BF16 values stored as float32, or FP32 dO).  Every (batch, head) slice is
+handled on its own so memory stays at a few N x N float64 matrices.
+
+Pinned by tests/test_oracle_attention64.py: brute-force scalar loops on tiny
+shapes, closed forms (zero queries give running means, row 0 of a causal
+product copies V[0]), softmax rows summing to one, central finite differences
+of sum(dO o O) for every gradient, the delta identity and the dQ identity.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F64 = np.float64
+
+
+def _slices(x):
+    lead = x.shape[:-2]
+    return lead, int(np.prod(lead)) if lead else 1
+
+
+def _scores(q, k, causal, scale):
+    s = (q @ k.T) * F64(scale)
+    if causal:
+        n = s.shape[0]
+        s[np.triu_indices(n, 1, s.shape[1])] = -np.inf
+    return s
+
+
+def _softmax_rows(s):
+    m = np.max(s, axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    z = np.sum(e, axis=-1, keepdims=True)
+    return e / z, (m + np.log(z))[..., 0]
+
+
+def fwd_slice(q, k, v, causal, scale):
+    """One (batch, head) slice: returns O [N,d], LSE [N], P [N,N] (float64)."""
+    q = np.asarray(q, F64)
+    k = np.asarray(k, F64)
+    v = np.asarray(v, F64)
+    s = _scores(q, k, causal, scale)
+    p, lse = _softmax_rows(s)
+    return p @ v, lse, p
+
+
+def bwd_slice(q, k, v, do, causal, scale, o=None):
+    """One slice of the backward.  Returns dict with dq, dk, dv, delta, delta_p.
+
+    delta uses O (the given one, or the exact O when o is None); delta_p is the
+    equivalent rowsum(dP o P), which the pages report as the stabilising
+    alternative (section 3.4.2).
+    """
+    q = np.asarray(q, F64)
+    k = np.asarray(k, F64)
+    v = np.asarray(v, F64)
+    do = np.asarray(do, F64)
+    o_exact, _, p = fwd_slice(q, k, v, causal, scale)
+    o_used = o_exact if o is None else np.asarray(o, F64)
+    dv = p.T @ do
+    dp = do @ v.T
+    delta = np.sum(do * o_used, axis=-1)
+    delta_p = np.sum(dp * p, axis=-1)
+    ds = p * (dp - delta[:, None])
+    dq = F64(scale) * (ds @ k)
+    dk = F64(scale) * (ds.T @ q)
+    return dict(dq=dq, dk=dk, dv=dv, delta=delta, delta_p=delta_p, p=p, o=o_exact)
+
+
+def attention_fwd(q, k, v, causal=True, scale=None):
+    """Batched forward over leading dims.  Returns (O, LSE) in float64."""
+    q = np.asarray(q)
+    d = q.shape[-1]
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    lead, nsl = _slices(q)
+    n = q.shape[-2]
+    qs, ks, vs = (x.reshape(nsl, x.shape[-2], x.shape[-1]) for x in (q, k, v))
+    o = np.empty((nsl, n, vs.shape[-1]), F64)
+    lse = np.empty((nsl, n), F64)
+    for i in range(nsl):
+        o[i], lse[i], _ = fwd_slice(qs[i], ks[i], vs[i], causal, scale)
+    return o.reshape(*lead, n, vs.shape[-1]), lse.reshape(*lead, n)
+
+
+def attention_bwd(q, k, v, do, causal=True, scale=None, o=None):
+    """Batched backward.  Returns dict of float64 arrays dq, dk, dv, delta, delta_p.
+
+    o: optional output to form delta = rowsum(dO o O) with (e.g. the BF16 O of
+    a kernel); by default the exact O is used.
+    """
+    q = np.asarray(q)
+    d = q.shape[-1]
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    lead, nsl = _slices(q)
+    n = q.shape[-2]
+    rs = lambda x: None if x is None else np.asarray(x).reshape(nsl, x.shape[-2], x.shape[-1])
+    qs, ks, vs, dos, os_ = rs(q), rs(k), rs(v), rs(do), rs(o)
+    out = {key: [] for key in ("dq", "dk", "dv", "delta", "delta_p")}
+    for i in range(nsl):
+        r = bwd_slice(qs[i], ks[i], vs[i], dos[i], causal, scale,
+                      None if os_ is None else os_[i])
+        for key in out:
+            out[key].append(r[key])
+    res = {}
+    for key, vals in out.items():
+        arr = np.stack(vals)
+        res[key] = arr.reshape(*lead, *arr.shape[1:])
+    return res
+
+
+def flops_fwd_bwd(b, h, n, d, causal=True):
+    """Algorithmic FLOPs of forward + backward: 2 products forward, 5 backward
+    (the S recompute, dP, dV, dK, dQ), each 2*N*N*d, halved when causal."""
+    f = 7 * 2 * b * h * n * n * d
+    return f // 2 if causal else f

@@ -1,0 +1,239 @@
+"""Part B of the oracle: BF16-emulating tiled flash attention forward.
+
+TEST INFRASTRUCTURE ONLY.  Follows, step by step and in the pages' order, the
+tiled forward pass of flash attention with the online safe softmax (the
+modified safe softmax of Algorithm 3 in section 3.4.5 of the paper-graph-ui
+summary of arXiv 2510.04212), rounding every intermediate the way a BF16
+kernel with FP32 accumulation does.  Rows are independent, so any subset of
+query rows can be emulated (all rows for small shapes, tied rows plus a sample
+for long sequences).
+
+Per query row T and per key tile j of width bn (keys t, masked when t > T in
+causal attention), starting from M = M2 = m = -inf, l = 0, Obar = 0:
+
+ 1. x_t = fp32(q_T . k_t)  (the dot of BF16 vectors in float64, then rounded);
+    S_t = fp32(x_t * fp32(scale)).  S is the softmax input the pages call S.
+ 2. Merge the tile's scores into the running top two of the row, as a
+    multiset: M is the largest score so far, M2 the second largest (equal to M
+    when the maximum occurs twice).  The tie flag is fp32(M - M2) <= fp32(eps)
+    -- "rs = rowsum(rm - S <= eps) > 1" of section 3.4.5, kept exactly across
+    tiles, so the final flag equals the untiled rule.
+ 3. Shift m: plain modes use m = M.  The tie-aware mode uses
+    m = fp32(beta * M) when the flag is set and M > 0, m = 0 when the flag is
+    set and M < 0, and m = M otherwise (section 3.4.5, the two "where" lines).
+ 4. alpha = exp(m_old - m_new) in FP32 (0 on the first tile).
+ 5. p_t = exp(fp32(S_t - m_new)) in FP32.
+ 6. P-bar_t = bf16(p_t) in the BF16 modes.  In the FP32-output mode the
+    product uses the high-precision P-bar: hi + lo with hi = bf16(p),
+    lo = bf16(p - hi)  (section 3.4.4, "computing only O-bar = P-bar V in FP32
+    is sufficient to stabilize training").
+ 7. l = fp32(alpha * l + sum_t P-bar_t) and Obar = fp32(alpha * Obar +
+    sum_t P-bar_t v_t): FP32 accumulation, each tile's sum formed exactly and
+    rounded once.  l sums the same P-bar that multiplies V, as in the pages'
+    O = Obar / rowsum(P-bar).
+ 8. Epilogue.  BF16 modes: Obar is rounded to BF16 once ("compute the dot
+    product in FP32, then round the final result to BF16", section 3.4.4) and
+    O = bf16(fp32(bf16(Obar) / l)).  FP32-output mode: O = fp32(Obar / l).
+    LSE = fp32(m + log l).  The output flag is the flag after the last tile.
+
+Readings where the pages leave a step open (listed with reasons in the design
+notes): the single BF16 rounding of Obar after FP32 accumulation over all tiles
+(step 8), l from the same rounded P-bar (step 7), the hi/lo P-bar of the FP32
+output mode (step 6), and the row-global running tie flag (step 2).
+
+With exact=True every rounding is switched off and all arithmetic is float64;
+the result must then equal plain attention in every mode (the shift invariance
+of section 3.4.5).  That is one of the pins in tests/test_oracle_flash_emu.py.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+from .numerics import bf16_rne, f32
+
+F64 = np.float64
+F32 = np.float32
+
+MODES = ("bf16_out", "fp32_out", "tie_aware_softmax")
+
+
+class _Round:
+    """The rounding steps of the BF16 kernel, or identities in exact mode."""
+
+    def __init__(self, exact: bool):
+        self.exact = exact
+
+    def r32(self, x):
+        return np.asarray(x, F64) if self.exact else f32(x).astype(F64)
+
+    def bf(self, x):
+        return np.asarray(x, F64) if self.exact else bf16_rne(f32(x)).astype(F64)
+
+    def exp(self, x):
+        x = np.asarray(x, F64)
+        if self.exact:
+            return np.exp(x)
+        with np.errstate(under="ignore", over="ignore"):
+            return np.exp(x.astype(F32)).astype(F64)
+
+    def log(self, x):
+        x = np.asarray(x, F64)
+        if self.exact:
+            with np.errstate(divide="ignore"):
+                return np.log(x)
+        with np.errstate(divide="ignore"):
+            return np.log(x.astype(F32)).astype(F64)
+
+
+@dataclass
+class EmuResult:
+    o: np.ndarray          # [S, R, d]  output (BF16 values or FP32 values, as float64)
+    lse: np.ndarray        # [S, R]
+    flag: np.ndarray       # [S, R] bool, final tie flag
+    row_max: np.ndarray    # [S, R] M, the row maximum of S
+    row_max2: np.ndarray   # [S, R] M2, second largest (multiset)
+    m_final: np.ndarray    # [S, R] the shift in force after the last tile
+    obar: np.ndarray       # [S, R, d] FP32 accumulator before the epilogue
+    l: np.ndarray          # [S, R] FP32 row sum of P-bar
+    n_pbar_one: np.ndarray  # [S, R] number of P-bar entries exactly equal to 1
+    max_pbar_flagged: np.ndarray  # [S, R] max P-bar over the tiles processed while the flag was set (-1 if none)
+
+
+def _top2_multiset(s):
+    """Largest and second largest along the last axis (multiset), -inf padded."""
+    if s.shape[-1] == 1:
+        return s[..., 0], np.full(s.shape[:-1], -np.inf)
+    part = -np.partition(-s, 1, axis=-1)[..., :2]
+    return part[..., 0], part[..., 1]
+
+
+def flash_forward(q, k, v, mode="bf16_out", causal=True, scale=None, bn=64,
+                  beta=2.0, eps=1e-3, q_pos=None, exact=False) -> EmuResult:
+    """Emulated tiled forward.
+
+    q: [S, R, d] query rows (BF16 values), k, v: [S, N, d] (BF16 values).
+    q_pos: [R] or [S, R] query positions of the rows (default arange(R), i.e.
+    all rows of an N = R sequence); used for the causal mask.
+    Leading dims other than one slice dim must be flattened by the caller.
+    """
+    if mode not in MODES:
+        raise ValueError(f"unknown mode {mode!r}")
+    rd = _Round(exact)
+    q = np.asarray(q, F64)
+    k = np.asarray(k, F64)
+    v = np.asarray(v, F64)
+    if q.ndim == 2:
+        q, k, v = q[None], k[None], v[None]
+    ns, r, d = q.shape
+    n = k.shape[1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    if q_pos is None:
+        q_pos = np.arange(r)
+    q_pos = np.broadcast_to(np.asarray(q_pos), (ns, r))
+    s_scale = rd.r32(scale)
+    eps_r = rd.r32(eps)
+    beta_r = rd.r32(beta)
+    tie_mode = mode == "tie_aware_softmax"
+    hp = mode == "fp32_out"
+
+    big_m = np.full((ns, r), -np.inf)
+    big_m2 = np.full((ns, r), -np.inf)
+    m = np.full((ns, r), -np.inf)
+    el = np.zeros((ns, r))
+    obar = np.zeros((ns, r, v.shape[2]))
+    n_one = np.zeros((ns, r), np.int64)
+    flag = np.zeros((ns, r), bool)
+    max_after = np.full((ns, r), -1.0)
+
+    for j0 in range(0, n, bn):
+        j1 = min(n, j0 + bn)
+        if causal and j0 > q_pos.max():
+            break
+        kt = k[:, j0:j1]
+        vt = v[:, j0:j1]
+        x = rd.r32(np.matmul(q, kt.transpose(0, 2, 1)))
+        s = rd.r32(x * s_scale)
+        if causal:
+            keys = np.arange(j0, j1)
+            s = np.where(keys[None, None, :] > q_pos[:, :, None], -np.inf, s)
+        # step 2: running top two (multiset) and the tie flag
+        t1, t2 = _top2_multiset(s)
+        cand = np.stack([big_m, big_m2, t1, t2], axis=-1)
+        big_m, big_m2 = _top2_multiset(cand)
+        with np.errstate(invalid="ignore"):
+            gap = rd.r32(big_m - big_m2)
+        flag = np.isfinite(big_m2) & (gap <= eps_r)
+        # step 3: the shift
+        if tie_mode:
+            m_new = np.where(flag & (big_m > 0), rd.r32(beta_r * big_m),
+                             np.where(flag & (big_m < 0), 0.0, big_m))
+        else:
+            m_new = big_m.copy()
+        # step 4: rescale factor for the earlier tiles
+        with np.errstate(invalid="ignore"):
+            alpha = np.where(np.isfinite(m), rd.exp(rd.r32(m - m_new)), 0.0)
+        # rows whose keys in this tile are all masked keep their state
+        active = np.isfinite(t1)
+        alpha = np.where(active, alpha, 1.0)
+        m_use = np.where(active, m_new, 0.0)
+        # step 5-6: probabilities and the P-bar that enters the product
+        with np.errstate(invalid="ignore"):
+            p = rd.exp(rd.r32(s - m_use[..., None]))
+        p = np.where(np.isfinite(s), p, 0.0)
+        if hp and not rd.exact:
+            hi = rd.bf(p)
+            lo = rd.bf(rd.r32(p - hi))
+            pbar = hi + lo
+        elif hp:
+            pbar = p
+        else:
+            pbar = rd.bf(p)
+        n_one += np.sum(pbar == 1.0, axis=-1)
+        tile_max = np.max(pbar, axis=-1)
+        max_after = np.where(flag & active, np.maximum(max_after, tile_max), max_after)
+        # step 7: FP32 accumulation, one rounding per tile
+        el = np.where(active, rd.r32(alpha * el + np.sum(pbar, axis=-1)), el)
+        obar_new = rd.r32(alpha[..., None] * obar + np.matmul(pbar, vt))
+        obar = np.where(active[..., None], obar_new, obar)
+        m = np.where(active, m_new, m)
+
+    # step 8: epilogue
+    with np.errstate(divide="ignore", invalid="ignore"):
+        if hp or rd.exact:
+            o = rd.r32(obar / el[..., None])
+        else:
+            ob = rd.bf(obar)
+            o = rd.bf(rd.r32(ob / el[..., None]))
+        lse = rd.r32(m + rd.log(el))
+    return EmuResult(o=o, lse=lse, flag=flag, row_max=big_m, row_max2=big_m2,
+                     m_final=m, obar=obar, l=el, n_pbar_one=n_one,
+                     max_pbar_flagged=max_after)
+
+
+def tie_flags_untiled(q, k, causal=True, scale=None, eps=1e-3, q_pos=None):
+    """The pages' untiled rule: rs = rowsum(rm - S <= eps), flag = rs > 1.
+
+    S is rounded exactly as in flash_forward step 1.  Returns (flag, rs).
+    """
+    q = np.asarray(q, F64)
+    k = np.asarray(k, F64)
+    if q.ndim == 2:
+        q, k = q[None], k[None]
+    ns, r, d = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    if q_pos is None:
+        q_pos = np.arange(r)
+    q_pos = np.broadcast_to(np.asarray(q_pos), (ns, r))
+    s = f32(f32(np.matmul(q, k.transpose(0, 2, 1))).astype(F64) * f32(scale).astype(F64)).astype(F64)
+    if causal:
+        keys = np.arange(k.shape[1])
+        s = np.where(keys[None, None, :] > q_pos[:, :, None], -np.inf, s)
+    rm = np.max(s, axis=-1, keepdims=True)
+    with np.errstate(invalid="ignore"):
+        diff = f32(rm - s).astype(F64)
+    rs = np.sum(np.isfinite(s) & (diff <= float(f32(eps))), axis=-1)
+    return rs > 1, rs

@@ -1,0 +1,127 @@
+"""Pins of oracle/attention64.py (Part A, float64 attention)."""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import attention64 as a64
+
+
+def _loops_forward(q, k, v, causal, scale):
+    """Scalar loops: weights exp(s) / sum exp(s) without any max subtraction."""
+    n, d = q.shape
+    o = np.zeros((n, v.shape[1]))
+    lse = np.zeros(n)
+    for i in range(n):
+        w = []
+        for j in range(k.shape[0]):
+            if causal and j > i:
+                w.append(0.0)
+                continue
+            s = sum(float(q[i, c]) * float(k[j, c]) for c in range(d)) * scale
+            w.append(math.exp(s))
+        z = sum(w)
+        lse[i] = math.log(z)
+        for j, wj in enumerate(w):
+            o[i] += (wj / z) * v[j]
+    return o, lse
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("n,d", [(1, 3), (5, 4), (8, 2)])
+def test_forward_matches_scalar_loops(causal, n, d):
+    rng = np.random.default_rng(n * 10 + d)
+    q, k, v = (rng.standard_normal((n, d)) for _ in range(3))
+    o, lse = a64.attention_fwd(q[None], k[None], v[None], causal=causal, scale=0.7)
+    o2, lse2 = _loops_forward(q, k, v, causal, 0.7)
+    np.testing.assert_allclose(o[0], o2, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse[0], lse2, rtol=0, atol=1e-13)
+
+
+def test_closed_forms():
+    rng = np.random.default_rng(0)
+    n, d = 9, 4
+    v = rng.standard_normal((n, d))
+    k = rng.standard_normal((n, d))
+    zq = np.zeros((n, d))
+    o, lse = a64.attention_fwd(zq, k, v, causal=True, scale=1.0)
+    # zero queries: every visible key has the same weight -> running means
+    want = np.cumsum(v, axis=0) / np.arange(1, n + 1)[:, None]
+    np.testing.assert_allclose(o, want, atol=1e-14)
+    np.testing.assert_allclose(lse, np.log(np.arange(1, n + 1)), atol=1e-14)
+    o, _ = a64.attention_fwd(zq, k, v, causal=False, scale=1.0)
+    np.testing.assert_allclose(o, np.broadcast_to(v.mean(0), o.shape), atol=1e-14)
+    # causal row 0 sees one key: O[0] = V[0], and its query gets no gradient
+    q = rng.standard_normal((n, d))
+    o, _ = a64.attention_fwd(q, k, v, causal=True, scale=0.5)
+    np.testing.assert_allclose(o[0], v[0], atol=1e-15)
+    g = a64.attention_bwd(q, k, v, rng.standard_normal((n, d)), causal=True, scale=0.5)
+    assert np.abs(g["dq"][0]).max() < 1e-15
+
+
+def test_softmax_rows_sum_to_one():
+    rng = np.random.default_rng(1)
+    q, k, v = (rng.standard_normal((64, 16)) * 3 for _ in range(3))
+    _, _, p = a64.fwd_slice(q, k, v, True, 0.25)
+    np.testing.assert_allclose(p.sum(-1), 1.0, atol=1e-12)
+    assert np.all(np.triu(p, 1) == 0)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_gradients_match_finite_differences(causal):
+    rng = np.random.default_rng(2)
+    n, d = 6, 3
+    q, k, v, do = (rng.standard_normal((n, d)) for _ in range(4))
+    scale = 0.8
+
+    def loss(q_, k_, v_):
+        o, _ = a64.attention_fwd(q_, k_, v_, causal=causal, scale=scale)
+        return float(np.sum(do * o))
+
+    g = a64.attention_bwd(q, k, v, do, causal=causal, scale=scale)
+    h = 1e-6
+    for name, x in (("dq", q), ("dk", k), ("dv", v)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp = x.copy()
+            xm = x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = [q, k, v]
+            args_m = [q, k, v]
+            pos = {"dq": 0, "dk": 1, "dv": 2}[name]
+            args_p[pos] = xp
+            args_m[pos] = xm
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        np.testing.assert_allclose(g[name], num, atol=2e-8, rtol=1e-6)
+
+
+def test_delta_identity():
+    """rowsum(dO o O) equals rowsum(dP o P) (section 3.4.2)."""
+    rng = np.random.default_rng(4)
+    q, k, v, do = (rng.standard_normal((32, 8)) for _ in range(4))
+    g = a64.attention_bwd(q, k, v, do, causal=True, scale=0.35)
+    np.testing.assert_allclose(g["delta"], g["delta_p"], atol=1e-12)
+
+
+def test_dq_error_identity():
+    """dQ_hp - dQ_lp = scale * diag(delta_lp - delta_hp) (P K)  (section 3.4.3)."""
+    rng = np.random.default_rng(5)
+    n, d = 16, 8
+    q, k, v, do = (rng.standard_normal((n, d)) for _ in range(4))
+    scale = 0.3
+    o_hp, _ = a64.attention_fwd(q, k, v, causal=True, scale=scale)
+    o_lp = o_hp + 1e-2 * rng.standard_normal(o_hp.shape)   # a perturbed (low-precision) O
+    g_hp = a64.attention_bwd(q, k, v, do, causal=True, scale=scale, o=o_hp)
+    g_lp = a64.attention_bwd(q, k, v, do, causal=True, scale=scale, o=o_lp)
+    _, _, p = a64.fwd_slice(q, k, v, True, scale)
+    want = scale * (g_lp["delta"] - g_hp["delta"])[:, None] * (p @ k)
+    np.testing.assert_allclose(g_hp["dq"] - g_lp["dq"], want, atol=1e-13)
+    # dK and dV: dV does not use delta; dK changes by scale * (diag(delta_lp - delta_hp) P)^T Q
+    np.testing.assert_allclose(g_hp["dv"], g_lp["dv"], atol=1e-14)
+    want_k = scale * (p * (g_lp["delta"] - g_hp["delta"])[:, None]).T @ q
+    np.testing.assert_allclose(g_hp["dk"] - g_lp["dk"], want_k, atol=1e-13)
+
+
+def test_flop_count():
+    assert a64.flops_fwd_bwd(1, 16, 8192, 128) == 962072674304
