@@ -1,0 +1,196 @@
+"""Benchmark: attention forward + backward throughput on one MI355X.
+
+One step = attn_fwd + the three backward stages (attn_bwd_prep, attn_bwd_main,
+attn_bwd_finish) over one batch of synthetic inputs already resident in HBM:
+the long-context workload B=1, H=16, N=8192, d=128, causal (the headline
+throughput configuration).  Throughput counts the algorithmic FLOPs
+7 * B * H * N^2 * d (forward: S = QK^T and P-bar V; backward: the S recompute,
+dP, dV, dK, dQ; each 2 N^2 d per head, halved by the causal mask).
+
+Prints ONE JSON line on stdout.  Each stage is a single kernel launch, timed
+with HIP events on the stream it runs on; the roofline object reports the
+kernel with the largest average duration.  The CPU baseline times the float64
+oracle (forward + backward) on (batch, head) slices of the same workload, as many
+as fit in about 12 seconds.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense BF16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+HBM_PEAK_GBS = 8000.0
+METRIC = "attention fwd+bwd TFLOP/s and % of bf16 MFMA peak; mean signed O error on tied rows"
+CSRC = os.path.join(ROOT, "precision_flash_attention_attn_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel: str):
+    """HBM bytes per launch measured with rocprofv3 counters, if they were taken
+    on the current kernel sources (else None)."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != source_hash():
+        return None
+    ent = t.get("kernels", {}).get(kernel)
+    return None if ent is None else ent.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, wl, budget_s=12.0):
+    """The float64 oracle (forward + backward) on (batch, head) slices of the
+    workload, one after another until about budget_s seconds have passed."""
+    from oracle import attention64 as a64
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count() or 1
+    nsl = wl.b * wl.h
+    done = 0
+    t0 = time.perf_counter()
+    while done < nsl and (time.perf_counter() - t0) < budget_s:
+        b, h = divmod(done, wl.h)
+        a64.slice_reference(inp.q[b, h], inp.k[b, h], inp.v[b, h], inp.do_bf16[b, h], causal=True,
+                            scale=wl.scale)
+        done += 1
+    dt = time.perf_counter() - t0
+    flops = done * 7 * wl.n * wl.n * wl.d  # algorithmic FLOPs of the slices done (causal)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {nsl} (batch, head) slices, N={wl.n} d={wl.d}, causal, "
+                      f"float64 numpy forward+backward, {dt:.1f} s"}
+
+
+def run_mode(torch, pfa, inp, wl, mode, steps, warmup):
+    dev = "cuda:0"
+    to = lambda x: torch.from_numpy(x).to(dev)
+    q, k, v = (to(x).to(torch.bfloat16).contiguous() for x in (inp.q, inp.k, inp.v))
+    io = torch.float32 if mode == "fp32_out" else torch.bfloat16
+    do = (to(inp.do_f32) if mode == "fp32_out" else to(inp.do_bf16).to(torch.bfloat16)).contiguous()
+    B, H, N, d = q.shape
+    o = torch.empty((B, H, N, d), device=dev, dtype=io)
+    lse = torch.empty((B, H, N), device=dev, dtype=torch.float32)
+    flags = torch.empty((B, H, N), device=dev, dtype=torch.int32)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    ws = torch.empty(pfa.attn_bwd_workspace_bytes(B, H, N, d, mode), device=dev, dtype=torch.uint8)
+    stream = torch.cuda.current_stream()
+    stages = ("fwd", "bwd_prep", "bwd_main", "bwd_finish")
+    calls = {
+        "fwd": lambda: pfa.attn_fwd(q, k, v, o, lse, flags, causal=True, mode=mode, stream=stream),
+        "bwd_prep": lambda: pfa.attn_bwd_prep(o, do, ws, mode=mode, stream=stream),
+        "bwd_main": lambda: pfa.attn_bwd_main(q, k, v, do, lse, dk, dv, ws, causal=True, mode=mode,
+                                              stream=stream),
+        "bwd_finish": lambda: pfa.attn_bwd_finish(dq, ws, stream=stream),
+    }
+    for _ in range(warmup):
+        for s in stages:
+            calls[s]()
+    torch.cuda.synchronize()
+    ev = {s: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)] for s in stages}
+    t0 = time.perf_counter()
+    for i in range(steps):
+        for s in stages:
+            ev[s][i][0].record(stream)
+            calls[s]()
+            ev[s][i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    avg_ms = {s: sum(a.elapsed_time(b) for a, b in ev[s]) / steps for s in stages}
+    ties = int(flags.sum().item())
+    return wall / steps * 1e3, avg_ms, ties
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--mode", default="bf16_out", choices=("bf16_out", "fp32_out", "tie_aware_softmax"))
+    ap.add_argument("--workload", type=int, default=4, help="synthetic workload id (4 = long context)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-tie", action="store_true", help="skip the tie-aware mode timing")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the (batch, head) slices would shard across GPUs with no exchange); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np  # noqa: F401
+    import torch
+
+    import precision_flash_attention_attn_amd as pfa
+    from synth.inputs import generate, workload
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    pfa.lib()  # fail loudly if the HIP library is missing
+    wl = workload(args.workload)
+    inp = generate(wl)
+    flops = wl.flops()
+    # forward: two products (S = QK^T, P-bar V) of 2 N^2 d each per head, halved by the mask
+    fwd_flops = 4 * wl.b * wl.h * wl.n * wl.n * wl.d // (2 if wl.causal else 1)
+    bwd_flops = flops - fwd_flops
+
+    ms, phases, ties = run_mode(torch, pfa, inp, wl, args.mode, args.steps, args.warmup)
+    value = flops / (ms * 1e-3) / 1e12
+
+    kern_flops = {"fwd": fwd_flops, "bwd_main": bwd_flops}
+    kname = {"fwd": "fwd_kernel", "bwd_main": "bwd_main_kernel"}
+    dom = max(kern_flops, key=lambda s: phases[s])
+    achieved = kern_flops[dom] / (phases[dom] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": stored_traffic(kname[dom]), "kernel": kname[dom],
+                "avg_launch_ms": round(phases[dom], 4),
+                "algorithmic_flops_per_launch": kern_flops[dom]}
+
+    extra = {"phases_ms": {s: round(t, 4) for s, t in phases.items()},
+             "tie_rows": ties,
+             "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+             "fwd_tflops": round(fwd_flops / (phases["fwd"] * 1e-3) / 1e12, 2),
+             "bwd_tflops": round(bwd_flops / (sum(phases[s] for s in phases if s != "fwd") * 1e-3) / 1e12, 2)}
+    if not args.no_tie and args.mode != "tie_aware_softmax":
+        ms_t, ph_t, _ = run_mode(torch, pfa, inp, wl, "tie_aware_softmax", args.steps, args.warmup)
+        extra["tie_aware_softmax"] = {"value": round(flops / (ms_t * 1e-3) / 1e12, 2),
+                                      "ms_per_step": round(ms_t, 4),
+                                      "phases_ms": {s: round(t, 4) for s, t in ph_t.items()}}
+
+    out = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic",
+           "config": {"workload": f"{wl.name}: B{wl.b} H{wl.h} N{wl.n} d{wl.d} causal, "
+                                  f"mode {args.mode}, {wl.note}",
+                      "batch": wl.b, "heads": wl.h, "seq_len": wl.n, "head_dim": wl.d,
+                      "causal": wl.causal, "mode": args.mode, "parallelism": "single GPU"},
+           "roofline": roofline}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, wl)
+    out.update(extra)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

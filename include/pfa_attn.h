@@ -1,0 +1,161 @@
+/*
+ * pfa_attn.h -- C ABI of the precision flash attention library (MI355X, gfx950).
+ *
+ * Tiled flash attention with the online safe softmax, forward and backward,
+ * BF16 inputs with FP32 accumulation, in three modes:
+ *
+ *   PFA_BF16_OUT            plain BF16 flash attention.  The unnormalised
+ *                           product O-bar = P-bar V is accumulated in FP32 over
+ *                           all key tiles, rounded to BF16 once, and the output
+ *                           O = O-bar / rowsum(P-bar) is rounded to BF16.
+ *                           P-bar = exp(S - rowmax S) is rounded to BF16 before
+ *                           the product, so P-bar is exactly 1 at every row
+ *                           maximum ("Why Low-Precision Transformer Training
+ *                           Fails", arXiv 2510.04212, as summarised on
+ *                           paper-graph-ui, section 3.4.4).
+ *   PFA_FP32_OUT            remedy 1: O is kept in FP32 and P-bar enters the
+ *                           product at high precision (a two-term BF16
+ *                           expansion hi + lo), section 3.4.2 "compute O in high
+ *                           precision" and section 3.4.4 "computing only
+ *                           O-bar = P-bar V in FP32".  dO is FP32 in this mode.
+ *   PFA_TIE_AWARE_SOFTMAX   remedy 2: the repeated-maximum-aware safe softmax of
+ *                           section 3.4.5.  With rm the row maximum and
+ *                           rs = #{t : rm - S_t <= eps}, the shift is beta*rm
+ *                           when rm > 0 and rs > 1, 0 when rm < 0 and rs > 1,
+ *                           and rm otherwise, so no P-bar equals 1 on rows with
+ *                           repeated maxima.  Output as in PFA_BF16_OUT.
+ *
+ * Scores are S = scale * Q K^T; with causal != 0, key t is masked for query
+ * T when t > T.  The tie test uses this S (FP32, base e) and eps in FP32.
+ *
+ * Layout: every tensor is contiguous [B, H, N, d] (d fastest), row vectors
+ * [B, H, N] for LSE, delta and tie flags.  Q, K, V, dQ, dK, dV are BF16; O and
+ * dO are BF16 except in PFA_FP32_OUT, where they are FP32.  All pointers are
+ * DEVICE pointers owned by the caller, 16-byte aligned.  The library allocates
+ * no memory, keeps no state between calls and launches only on the given
+ * stream (a hipStream_t; NULL is the default stream).  Calls are asynchronous:
+ * a device fault surfaces at the caller's next synchronisation.
+ *
+ * Supported: d in {64, 128}; any N >= 1 (ragged tails are masked); B, H >= 1;
+ * B*H*N*d < 2^40.
+ *
+ * Errors: arguments are checked before anything is launched; a failed check
+ * returns a negative status and writes nothing.  PFA_ERR_INVALID for a NULL
+ * required pointer, misaligned pointer, non-positive or oversized B/H/N,
+ * non-finite or non-positive scale, unknown mode, beta <= 1 or non-finite,
+ * eps < 0 or non-finite, a too small workspace.  PFA_ERR_UNSUPPORTED for
+ * d not in {64, 128}.  PFA_ERR_HIP if a launch fails.
+ *
+ * Numerical note (tie-aware mode): when (beta - 1) * rm exceeds the FP32
+ * exponent range (about 87) on a tied row, every P-bar underflows, the row sum
+ * is 0 and that row of O is NaN.  The pages name this underflow as the reason
+ * the shift is applied only to tied rows; it is reported, not an error code.
+ */
+#ifndef PFA_ATTN_H
+#define PFA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum pfa_mode { PFA_BF16_OUT = 0, PFA_FP32_OUT = 1, PFA_TIE_AWARE_SOFTMAX = 2 };
+
+enum pfa_status {
+  PFA_OK = 0,
+  PFA_ERR_INVALID = -1,
+  PFA_ERR_UNSUPPORTED = -2,
+  PFA_ERR_HIP = -3
+};
+
+/* Parameters of the repeated-maximum-aware softmax (section 3.4.5): beta > 1
+ * (the pages use 2, and recommend 2 to 8), eps >= 0 (the pages' example is
+ * 1e-3).  NULL selects {2.0f, 1e-3f}. */
+typedef struct pfa_tie_opts {
+  float beta;
+  float eps;
+} pfa_tie_opts;
+
+/*
+ * Forward pass.  Defines: P-bar = exp(S - m), O-bar = P-bar V,
+ * O = O-bar / rowsum(P-bar)  (section 3.4.4), m chosen per mode as above.
+ *
+ *   q, k, v    in   BF16 [B,H,N,d]
+ *   o          out  BF16 [B,H,N,d] (PFA_FP32_OUT: FP32)
+ *   lse        out  FP32 [B,H,N], m + log(rowsum P-bar): the log of the
+ *                   softmax normaliser, used by the backward
+ *   tie_flags  out  INT32 [B,H,N] or NULL: 1 where at least two unmasked
+ *                   scores lie within eps of the row maximum (rs > 1), else 0.
+ *                   The same function of S in every mode.
+ *   opts       in   tie parameters (NULL = defaults); eps also sets the flag
+ *                   threshold in the plain modes.
+ *   stream     in   hipStream_t
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int32_t* tie_flags, int B, int H, int N, int d, int causal, float scale,
+             int mode, const pfa_tie_opts* opts, void* stream);
+
+/* Bytes of device workspace attn_bwd needs: an FP32 dQ accumulator and the
+ * FP32 delta row vector, each 256-byte aligned.  0 on invalid sizes. */
+size_t attn_bwd_workspace_bytes(int B, int H, int N, int d, int mode);
+
+/*
+ * Backward pass (section 3.4.2 and 3.4.3):
+ *   delta = rowsum(dO o O); P = exp(S - LSE); dV = P^T dO; dP = dO V^T;
+ *   dS = P o (dP - delta); dQ = scale * dS K; dK = scale * dS^T Q.
+ * The tie-aware softmax changes only the forward: given its O and LSE the
+ * backward is that of PFA_BF16_OUT.
+ *
+ *   q, k, v         in   BF16 [B,H,N,d]
+ *   o, dout         in   BF16 [B,H,N,d] (PFA_FP32_OUT: FP32)
+ *   lse             in   FP32 [B,H,N] from attn_fwd
+ *   dq, dk, dv      out  BF16 [B,H,N,d]
+ *   delta           out  FP32 [B,H,N] or NULL: delta as used, for diagnostics
+ *   workspace       in   device memory of at least attn_bwd_workspace_bytes;
+ *                        contents on entry are ignored (the library clears what
+ *                        it needs with a kernel, so the call can be captured in
+ *                        a HIP graph)
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, float* delta,
+             void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+             int causal, float scale, int mode, void* stream);
+
+/*
+ * The backward in its three stages, for callers that schedule or time them
+ * separately.  attn_bwd runs exactly these three on one stream; running them
+ * in order on one stream with the same workspace gives the same result.
+ *
+ * Stage 1, attn_bwd_prep: delta = rowsum(dO o O) in FP32 -- the term the
+ * pages single out as computed apart in the backward (section 3.4.2) -- into
+ * `delta` (or into the workspace when delta is NULL), and clears the FP32 dQ
+ * accumulator in the workspace.  o, dout: BF16 (FP32 in PFA_FP32_OUT).
+ */
+int attn_bwd_prep(const void* o, const void* dout, float* delta, void* workspace,
+                  size_t workspace_bytes, int B, int H, int N, int d, int mode, void* stream);
+
+/* Stage 2, attn_bwd_main: P = exp(S - LSE), dP = dO V^T,
+ * dS = P o (dP - delta); writes dV = P^T dO and dK = scale dS^T Q (BF16) and
+ * adds dS K into the FP32 dQ accumulator (sections 3.4.2, 3.4.3).  delta: the
+ * vector stage 1 wrote (NULL = the workspace copy). */
+int attn_bwd_main(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                  const float* delta, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                  int B, int H, int N, int d, int causal, float scale, int mode, void* stream);
+
+/* Stage 3, attn_bwd_finish: dQ = bf16(scale * accumulator). */
+int attn_bwd_finish(void* dq, const void* workspace, size_t workspace_bytes, int B, int H, int N,
+                    int d, float scale, void* stream);
+
+/* Static text for a status code. */
+const char* attn_strerror(int status);
+
+/* Library version string. */
+const char* attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PFA_ATTN_H */

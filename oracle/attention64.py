@@ -131,3 +131,47 @@ def flops_fwd_bwd(b, h, n, d, causal=True):
     (the S recompute, dP, dV, dK, dQ), each 2*N*N*d, halved when causal."""
     f = 7 * 2 * b * h * n * n * d
     return f // 2 if causal else f
+
+
+def slice_reference(q, k, v, do=None, causal=True, scale=None, o_for_delta=None, chunk=1024):
+    """Forward and backward of one (batch, head) slice in float64, query rows
+    taken `chunk` at a time so long sequences fit in memory.
+
+    Query rows are independent in the forward, in delta and in dQ; dK and dV
+    are sums over query rows and are accumulated chunk by chunk.  Same
+    definitions as fwd_slice / bwd_slice (pinned against them in the tests).
+    o_for_delta: the O used in delta = rowsum(dO o O) (default: the exact O).
+    Returns dict(o, lse, dq, dk, dv, delta) of float64 arrays.
+    """
+    q = np.asarray(q, F64)
+    k = np.asarray(k, F64)
+    v = np.asarray(v, F64)
+    n, d = q.shape
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    out = dict(o=np.empty((n, v.shape[1])), lse=np.empty(n))
+    if do is not None:
+        do = np.asarray(do, F64)
+        out.update(dq=np.empty((n, d)), dk=np.zeros_like(k), dv=np.zeros_like(v), delta=np.empty(n))
+    for r0 in range(0, n, chunk):
+        r1 = min(n, r0 + chunk)
+        kend = r1 if causal else k.shape[0]
+        s = (q[r0:r1] @ k[:kend].T) * F64(scale)
+        if causal:
+            rows = np.arange(r0, r1)[:, None]
+            s = np.where(np.arange(kend)[None, :] > rows, -np.inf, s)
+        p, lse = _softmax_rows(s)
+        o = p @ v[:kend]
+        out["o"][r0:r1] = o
+        out["lse"][r0:r1] = lse
+        if do is None:
+            continue
+        g = do[r0:r1]
+        o_used = o if o_for_delta is None else np.asarray(o_for_delta[r0:r1], F64)
+        dp = g @ v[:kend].T
+        delta = np.sum(g * o_used, axis=-1)
+        ds = p * (dp - delta[:, None])
+        out["dq"][r0:r1] = F64(scale) * (ds @ k[:kend])
+        out["dk"][:kend] += F64(scale) * (ds.T @ q[r0:r1])
+        out["dv"][:kend] += p.T @ g
+        out["delta"][r0:r1] = delta
+    return out

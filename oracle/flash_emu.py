@@ -213,10 +213,12 @@ def flash_forward(q, k, v, mode="bf16_out", causal=True, scale=None, bn=64,
                      max_pbar_flagged=max_after)
 
 
-def tie_flags_untiled(q, k, causal=True, scale=None, eps=1e-3, q_pos=None):
+def tie_flags_untiled(q, k, causal=True, scale=None, eps=1e-3, q_pos=None, return_gap=False):
     """The pages' untiled rule: rs = rowsum(rm - S <= eps), flag = rs > 1.
 
-    S is rounded exactly as in flash_forward step 1.  Returns (flag, rs).
+    S is rounded exactly as in flash_forward step 1.  Returns (flag, rs), and
+    with return_gap also the gap between the largest and second largest score
+    (multiset; inf where a row has a single unmasked key).
     """
     q = np.asarray(q, F64)
     k = np.asarray(k, F64)
@@ -236,4 +238,9 @@ def tie_flags_untiled(q, k, causal=True, scale=None, eps=1e-3, q_pos=None):
     with np.errstate(invalid="ignore"):
         diff = f32(rm - s).astype(F64)
     rs = np.sum(np.isfinite(s) & (diff <= float(f32(eps))), axis=-1)
-    return rs > 1, rs
+    if not return_gap:
+        return rs > 1, rs
+    top1, top2 = _top2_multiset(s)
+    with np.errstate(invalid="ignore"):
+        gap = np.where(np.isfinite(top2), f32(top1 - top2).astype(F64), np.inf)
+    return rs > 1, rs, gap, top1

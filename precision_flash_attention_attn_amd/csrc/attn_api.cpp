@@ -1,0 +1,196 @@
+// C ABI of the precision flash attention library: argument checks, then the
+// kernel launches on the caller's stream.  Every check runs before any HIP
+// call, so invalid arguments return an error without touching the device.
+#include <cmath>
+#include <cstdint>
+
+#include "pfa_attn.h"
+#include "pfa_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int check_sizes(int B, int H, int N, int d) {
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return PFA_ERR_INVALID;
+  const int64_t bh = int64_t(B) * H;
+  if (bh * N * d >= kMaxElems) return PFA_ERR_INVALID;
+  // grid sizes: (B*H) * ceil(N/128) workgroups must fit a 31-bit grid
+  if (bh * ((int64_t(N) + 127) / 128) >= (int64_t(1) << 31)) return PFA_ERR_INVALID;
+  if (d != 64 && d != 128) return PFA_ERR_UNSUPPORTED;
+  return PFA_OK;
+}
+
+int check_common(int B, int H, int N, int d, float scale, int mode) {
+  const int s = check_sizes(B, H, N, d);
+  if (s != PFA_OK) return s;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return PFA_ERR_INVALID;
+  if (mode != PFA_BF16_OUT && mode != PFA_FP32_OUT && mode != PFA_TIE_AWARE_SOFTMAX)
+    return PFA_ERR_INVALID;
+  return PFA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int32_t* tie_flags,
+             int B, int H, int N, int d, int causal, float scale, int mode,
+             const pfa_tie_opts* opts, void* stream) {
+  int st = check_common(B, H, N, d, scale, mode);
+  if (st != PFA_OK) return st;
+  if (!q || !k || !v || !o || !lse) return PFA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse))
+    return PFA_ERR_INVALID;
+  if (tie_flags && !aligned4(tie_flags)) return PFA_ERR_INVALID;
+  float beta = 2.0f, eps = 1e-3f;
+  if (opts) {
+    beta = opts->beta;
+    eps = opts->eps;
+  }
+  if (!std::isfinite(beta) || !(beta > 1.0f)) return PFA_ERR_INVALID;
+  if (!std::isfinite(eps) || !(eps >= 0.0f)) return PFA_ERR_INVALID;
+
+  pfa::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.flags = tie_flags;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.d = d;
+  a.causal = causal ? 1 : 0;
+  a.mode = mode;
+  a.scale = scale;
+  a.beta = beta;
+  a.eps = eps;
+  const hipError_t e = pfa::launch_fwd(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PFA_OK : PFA_ERR_HIP;
+}
+
+size_t attn_bwd_workspace_bytes(int B, int H, int N, int d, int mode) {
+  if (check_sizes(B, H, N, d) != PFA_OK) return 0;
+  if (mode != PFA_BF16_OUT && mode != PFA_FP32_OUT && mode != PFA_TIE_AWARE_SOFTMAX) return 0;
+  const size_t rows = size_t(B) * H * N;
+  return pfa::bwd_dq_acc_bytes(rows, d) + pfa::bwd_delta_bytes(rows);
+}
+
+namespace {
+
+// Shared checks of the backward entry points; fills the workspace pointers.
+int bwd_args(pfa::BwdArgs& a, void* workspace, size_t workspace_bytes, float* delta, int B, int H,
+             int N, int d, int causal, float scale, int mode) {
+  const int st = check_common(B, H, N, d, scale, mode);
+  if (st != PFA_OK) return st;
+  if (!workspace || !aligned16(workspace)) return PFA_ERR_INVALID;
+  if (delta && !aligned4(delta)) return PFA_ERR_INVALID;
+  const size_t need = attn_bwd_workspace_bytes(B, H, N, d, mode);
+  if (need == 0 || workspace_bytes < need) return PFA_ERR_INVALID;
+  const size_t rows = size_t(B) * H * N;
+  char* ws = static_cast<char*>(workspace);
+  a = pfa::BwdArgs{};
+  a.dq_acc = reinterpret_cast<float*>(ws);
+  a.delta = delta ? delta : reinterpret_cast<float*>(ws + pfa::bwd_dq_acc_bytes(rows, d));
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.d = d;
+  a.causal = causal ? 1 : 0;
+  a.mode = mode;
+  a.scale = scale;
+  return PFA_OK;
+}
+
+bool ok16(const void* p) { return p && aligned16(p); }
+
+int status_of(hipError_t e) { return e == hipSuccess ? PFA_OK : PFA_ERR_HIP; }
+
+}  // namespace
+
+int attn_bwd_prep(const void* o, const void* dout, float* delta, void* workspace,
+                  size_t workspace_bytes, int B, int H, int N, int d, int mode, void* stream) {
+  pfa::BwdArgs a;
+  const int st = bwd_args(a, workspace, workspace_bytes, delta, B, H, N, d, 1, 1.0f, mode);
+  if (st != PFA_OK) return st;
+  if (!ok16(o) || !ok16(dout)) return PFA_ERR_INVALID;
+  a.o = o;
+  a.dout = dout;
+  return status_of(pfa::launch_bwd_prep(a, static_cast<hipStream_t>(stream)));
+}
+
+int attn_bwd_main(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                  const float* delta, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                  int B, int H, int N, int d, int causal, float scale, int mode, void* stream) {
+  pfa::BwdArgs a;
+  const int st = bwd_args(a, workspace, workspace_bytes, const_cast<float*>(delta), B, H, N, d,
+                          causal, scale, mode);
+  if (st != PFA_OK) return st;
+  if (!ok16(q) || !ok16(k) || !ok16(v) || !ok16(dout) || !ok16(dk) || !ok16(dv)) return PFA_ERR_INVALID;
+  if (!lse || !aligned4(lse)) return PFA_ERR_INVALID;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  a.lse = lse;
+  a.dk = dk;
+  a.dv = dv;
+  return status_of(pfa::launch_bwd_main(a, static_cast<hipStream_t>(stream)));
+}
+
+int attn_bwd_finish(void* dq, const void* workspace, size_t workspace_bytes, int B, int H, int N,
+                    int d, float scale, void* stream) {
+  pfa::BwdArgs a;
+  const int st = bwd_args(a, const_cast<void*>(workspace), workspace_bytes, nullptr, B, H, N, d, 1,
+                          scale, PFA_BF16_OUT);
+  if (st != PFA_OK) return st;
+  if (!ok16(dq)) return PFA_ERR_INVALID;
+  a.dq = dq;
+  return status_of(pfa::launch_bwd_finish(a, static_cast<hipStream_t>(stream)));
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, float* delta, void* workspace,
+             size_t workspace_bytes, int B, int H, int N, int d, int causal, float scale, int mode,
+             void* stream) {
+  pfa::BwdArgs a;
+  int st = bwd_args(a, workspace, workspace_bytes, delta, B, H, N, d, causal, scale, mode);
+  if (st != PFA_OK) return st;
+  if (!ok16(q) || !ok16(k) || !ok16(v) || !ok16(o) || !ok16(dout) || !ok16(dq) || !ok16(dk) ||
+      !ok16(dv))
+    return PFA_ERR_INVALID;
+  if (!lse || !aligned4(lse)) return PFA_ERR_INVALID;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = pfa::launch_bwd_prep(a, s);
+  if (e == hipSuccess) e = pfa::launch_bwd_main(a, s);
+  if (e == hipSuccess) e = pfa::launch_bwd_finish(a, s);
+  return status_of(e);
+}
+
+const char* attn_strerror(int status) {
+  switch (status) {
+    case PFA_OK: return "ok";
+    case PFA_ERR_INVALID: return "invalid argument";
+    case PFA_ERR_UNSUPPORTED: return "unsupported configuration (head dimension must be 64 or 128)";
+    case PFA_ERR_HIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+const char* attn_version(void) { return "pfa_attn 0.1.0 gfx950"; }
+
+}  // extern "C"

@@ -1,0 +1,143 @@
+"""The C ABI library: loads, exports what include/pfa_attn.h declares, and
+rejects invalid arguments before launching anything (runs without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pfa_attn.h")
+
+pfa = pytest.importorskip("precision_flash_attention_attn_amd")
+from precision_flash_attention_attn_amd import _binding as bnd  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(bnd.LIB_PATH):
+        from precision_flash_attention_attn_amd.build import build_library
+        build_library()
+    return bnd.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(attn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    assert set(bnd.EXPORTED) == set(names)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+    assert L.attn_version().decode().startswith("pfa_attn")
+
+
+def test_strerror(L):
+    assert L.attn_strerror(0) == b"ok"
+    assert b"invalid" in L.attn_strerror(-1)
+    assert b"64 or 128" in L.attn_strerror(-2)
+    assert L.attn_strerror(12345) == b"unknown status"
+
+
+def test_workspace_bytes(L):
+    n = L.attn_bwd_workspace_bytes(1, 16, 8192, 128, 0)
+    rows = 16 * 8192
+    assert n == rows * 128 * 4 + rows * 4
+    assert L.attn_bwd_workspace_bytes(1, 1, 1, 64, 0) == 512          # two 256-byte-aligned parts
+    assert L.attn_bwd_workspace_bytes(1, 1, 1, 96, 0) == 0
+    assert L.attn_bwd_workspace_bytes(0, 1, 1, 64, 0) == 0
+    assert L.attn_bwd_workspace_bytes(1, 1, 1, 64, 7) == 0
+
+
+FAKE = 0x10000  # a 16-byte-aligned non-null address; never dereferenced (checks fail first)
+
+
+def _fwd(L, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, flags=None, B=1, H=1, N=128, d=64, causal=1,
+         scale=0.125, mode=0, opts=None):
+    return L.attn_fwd(q, k, v, o, lse, flags, B, H, N, d, causal, scale, mode,
+                      ctypes.byref(opts) if opts is not None else None, None)
+
+
+def test_fwd_rejects_invalid_arguments(L):
+    inv, uns = bnd.PFA_ERR_INVALID, bnd.PFA_ERR_UNSUPPORTED
+    assert _fwd(L, q=None) == inv
+    assert _fwd(L, lse=None) == inv
+    assert _fwd(L, o=FAKE + 8) == inv                      # misaligned
+    assert _fwd(L, flags=FAKE + 2) == inv                  # misaligned flags
+    assert _fwd(L, B=0) == inv
+    assert _fwd(L, N=-5) == inv
+    assert _fwd(L, d=96) == uns
+    assert _fwd(L, d=256) == uns
+    assert _fwd(L, scale=float("nan")) == inv
+    assert _fwd(L, scale=0.0) == inv
+    assert _fwd(L, scale=-1.0) == inv
+    assert _fwd(L, mode=3) == inv
+    assert _fwd(L, mode=-1) == inv
+    assert _fwd(L, opts=bnd.TieOpts(1.0, 1e-3)) == inv     # beta must exceed 1
+    assert _fwd(L, opts=bnd.TieOpts(float("inf"), 1e-3)) == inv
+    assert _fwd(L, opts=bnd.TieOpts(2.0, -1e-3)) == inv
+    assert _fwd(L, opts=bnd.TieOpts(2.0, float("nan"))) == inv
+    assert _fwd(L, B=1 << 16, H=1 << 16, N=1 << 10, d=128) == inv   # too many elements
+
+
+def _bwd(L, ws=FAKE, ws_bytes=1 << 30, q=FAKE, dq=FAKE, o=FAKE, B=1, H=1, N=128, d=64, mode=0,
+         scale=0.125, delta=None):
+    return L.attn_bwd(q, FAKE, FAKE, o, FAKE, FAKE, dq, FAKE, FAKE, delta, ws, ws_bytes,
+                      B, H, N, d, 1, scale, mode, None)
+
+
+def test_bwd_rejects_invalid_arguments(L):
+    inv, uns = bnd.PFA_ERR_INVALID, bnd.PFA_ERR_UNSUPPORTED
+    need = L.attn_bwd_workspace_bytes(1, 1, 128, 64, 0)
+    assert _bwd(L, ws=None) == inv
+    assert _bwd(L, ws_bytes=need - 1) == inv
+    assert _bwd(L, ws=FAKE + 4) == inv
+    assert _bwd(L, q=None) == inv
+    assert _bwd(L, dq=FAKE + 2) == inv
+    assert _bwd(L, o=None) == inv
+    assert _bwd(L, d=80) == uns
+    assert _bwd(L, mode=5) == inv
+    assert _bwd(L, scale=float("inf")) == inv
+    assert _bwd(L, delta=FAKE + 1) == inv
+
+
+def test_python_binding_validates_before_calling(L):
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)       # CPU tensor: rejected
+    with pytest.raises(ValueError):
+        pfa.forward(q, q, q)
+    with pytest.raises(ValueError):
+        pfa.attn_fwd(q, q, q, q, None, mode="bf16_out")
+    with pytest.raises(ValueError):
+        bnd._mode_id("fp16_out")
+
+
+def test_backward_stages_reject_invalid_arguments(L):
+    inv, uns = bnd.PFA_ERR_INVALID, bnd.PFA_ERR_UNSUPPORTED
+    need = L.attn_bwd_workspace_bytes(1, 1, 128, 64, 0)
+    assert L.attn_bwd_prep(FAKE, FAKE, None, FAKE, need - 16, 1, 1, 128, 64, 0, None) == inv
+    assert L.attn_bwd_prep(None, FAKE, None, FAKE, need, 1, 1, 128, 64, 0, None) == inv
+    assert L.attn_bwd_prep(FAKE, FAKE, None, FAKE, need, 1, 1, 128, 32, 0, None) == uns
+    assert L.attn_bwd_prep(FAKE, FAKE, FAKE + 2, FAKE, need, 1, 1, 128, 64, 0, None) == inv
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, need, 1, 1, 128, 64, 1, 0.125, 0, None]
+    bad = list(args)
+    bad[4] = None                                    # lse
+    assert L.attn_bwd_main(*bad) == inv
+    bad = list(args)
+    bad[7] = FAKE + 8                                # dv misaligned
+    assert L.attn_bwd_main(*bad) == inv
+    bad = list(args)
+    bad[15] = float("nan")                           # scale
+    assert L.attn_bwd_main(*bad) == inv
+    bad = list(args)
+    bad[16] = 9                                      # mode
+    assert L.attn_bwd_main(*bad) == inv
+    assert L.attn_bwd_finish(None, FAKE, need, 1, 1, 128, 64, 0.125, None) == inv
+    assert L.attn_bwd_finish(FAKE, FAKE, need, 1, 1, 128, 64, 0.0, None) == inv
+    assert L.attn_bwd_finish(FAKE, FAKE, need - 1, 1, 1, 128, 64, 0.125, None) == inv

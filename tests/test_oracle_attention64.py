@@ -125,3 +125,17 @@ def test_dq_error_identity():
 
 def test_flop_count():
     assert a64.flops_fwd_bwd(1, 16, 8192, 128) == 962072674304
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_row_chunked_reference_equals_whole_slice(causal):
+    rng = np.random.default_rng(9)
+    n, d = 70, 8
+    q, k, v, do = (rng.standard_normal((n, d)) for _ in range(4))
+    r = a64.slice_reference(q, k, v, do, causal=causal, scale=0.4, chunk=16)
+    o, lse, _ = a64.fwd_slice(q, k, v, causal, 0.4)
+    g = a64.bwd_slice(q, k, v, do, causal, 0.4)
+    np.testing.assert_allclose(r["o"], o, atol=1e-13)
+    np.testing.assert_allclose(r["lse"], lse, atol=1e-13)
+    for key in ("dq", "dk", "dv", "delta"):
+        np.testing.assert_allclose(r[key], g[key], atol=1e-12)
