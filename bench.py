@@ -129,6 +129,9 @@ def main():
     ap.add_argument("--workload", type=int, default=4, help="synthetic workload id (4 = long context)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-tie", action="store_true", help="skip the tie-aware mode timing")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB three times (for scaling the "
+                         "HBM byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -138,6 +141,16 @@ def main():
 
     import numpy as np  # noqa: F401
     import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
+        return
 
     import precision_flash_attention_attn_amd as pfa
     from synth.inputs import generate, workload

@@ -76,11 +76,27 @@ __device__ __forceinline__ void lds_write_b128(char* lds_base, int byte_off, con
   *reinterpret_cast<u32x4*>(lds_base + byte_off) = v;
 }
 
-// Swizzled byte offset of 16-byte chunk `chunk` of row `row` in a tile with
-// CHUNKS chunks per row (CHUNKS a power of two).
+// XOR pattern applied to the 16-byte chunk index of a row of a row-major BF16
+// tile in LDS (CHUNKS = 16-byte chunks per row: 16 for 128 features, 8 for
+// 64).  Two read patterns must both be free of bank conflicts:
+//  * 16 lanes reading one chunk from each of 16 different rows (MFMA operands
+//    read with ds_read_b128): the pattern is a permutation of the rows mod 16;
+//  * the transpose read: 4 consecutive rows (4-aligned) x 4 consecutive chunks
+//    (4-aligned): the pattern sends each of the 4 rows to its own 64-byte
+//    quad of banks.
+// 16 chunks: bits 0-1 of the row select the quad, bits 2-3 the chunk within it.
+// 8 chunks (two rows share a 256-byte bank line): bit 1 of the row selects the
+// quad, bits 2-3 the chunk.
+template <int CHUNKS>
+__device__ __forceinline__ int swz_pattern(int row) {
+  if (CHUNKS == 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+  return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
+
+// Swizzled byte offset of 16-byte chunk `chunk` of row `row`.
 template <int CHUNKS>
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return (row * CHUNKS + (chunk ^ (row & (CHUNKS - 1)))) * 16;
+  return (row * CHUNKS + (chunk ^ swz_pattern<CHUNKS>(row))) * 16;
 }
 
 // Byte offset of element (row, col) of a swizzled row-major BF16 tile.
