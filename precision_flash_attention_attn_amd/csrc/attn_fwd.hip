@@ -9,11 +9,12 @@
 // (the modified safe softmax inside the tiled forward pass).
 //
 // Work decomposition: one workgroup of 4 waves per (batch*head, block of 128
-// queries); each wave owns 32 queries.  Keys stream in tiles of 64 through a
-// double-buffered LDS stage.  Per tile and wave:
+// queries), two workgroups per CU; each wave owns 32 queries.  Keys stream in
+// tiles of 64 through a double-buffered LDS stage filled by direct
+// global->LDS loads.  Per tile and wave:
 //   S^T (64 keys x 32 queries) = K_tile Q^T   (MFMA, A = K rows from LDS,
 //                                              B = the wave's Q held in VGPRs)
-//   online max / top-2 / shift / exp on the accumulators (VALU)
+//   online row maximum / top-2 / shift / exp on the accumulators (VALU)
 //   O^T (d x 32 queries) += V_tile^T P-bar^T   (MFMA, A = V read transposed from
 //                                              LDS, B = P-bar packed to BF16 in
 //                                              place from the S accumulators)
@@ -21,6 +22,11 @@
 // sigma32) so that the accumulator registers of a lane already hold the 8
 // consecutive keys the P-bar V step needs as its B operand: P-bar never goes
 // through LDS.
+//
+// Scores are kept as the raw dot products q.k in the accumulators.  S =
+// fp32(dot * scale) is monotone in the dot, so the row maximum and the second
+// largest score of S are the scaled maximum and second largest dot; only those
+// two are scaled, which gives bit for bit the S-based tie test of the pages.
 #include "pfa_common.h"
 #include "pfa_internal.h"
 
@@ -62,200 +68,221 @@ __device__ __forceinline__ void map_block(int bid, int BH, int nqb, int& bh, int
 }
 
 template <int D, int MODE, bool CAUSAL, bool FLAGS>
-__global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
-  constexpr int BM = 128, BN = 64, NT = 256;
-  constexpr int CH = D / 8;    // 16-byte chunks per K/V row
-  constexpr int DC = D / 16;   // contraction steps of K Q^T
-  constexpr int KB = BN / 32;  // 32-key blocks per tile
-  constexpr int KC = BN / 16;  // 16-key contraction steps of V^T P^T
-  constexpr int DB = D / 32;   // 32-feature blocks of O
-  constexpr bool TIE = MODE == kTieAware;
-  constexpr bool HP = MODE == kFp32Out;
-  constexpr bool SUNITS = FLAGS || TIE;  // scores kept as S = scale*dot (else the raw dot)
-  constexpr int TILE_BYTES = BN * D * 2;
-  constexpr int ROWS_PER_PASS = NT / CH;
-  constexpr int PASSES = BN / ROWS_PER_PASS;
+struct FwdKernel {
+  static constexpr int BM = 128, BN = 64, NT = 256;
+  static constexpr int CH = D / 8;    // 16-byte chunks per K/V row
+  static constexpr int DC = D / 16;   // contraction steps of K Q^T
+  static constexpr int KB = BN / 32;  // 32-key blocks per tile
+  static constexpr int KC = BN / 16;  // 16-key contraction steps of V^T P^T
+  static constexpr int DB = D / 32;   // 32-feature blocks of O
+  static constexpr bool TIE = MODE == kTieAware;
+  static constexpr bool HP = MODE == kFp32Out;
+  static constexpr int TILE = BN * D * 2;            // bytes of one K (or V) tile
+  static constexpr int LOADS = TILE / (NT * 16);     // direct loads per thread per tile and tensor
+  static constexpr int ROWB = CH * 16;               // bytes per LDS row
 
-  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * TILE_BYTES];
-
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hi = lane >> 5;
-  const int N = p.N;
-  int bh, qb;
-  map_block(blockIdx.x, p.BH, p.n_qblocks, bh, qb);
-  const size_t base = (size_t)bh * N * D;
-  const uint16_t* __restrict__ Q = p.q + base;
-  const uint16_t* __restrict__ K = p.k + base;
-  const uint16_t* __restrict__ V = p.v + base;
-  const int q0 = qb * BM;
-  const int qw0 = q0 + 32 * w;
-  const int myq = qw0 + (lane & 31);
-
-  // This wave's queries as the B operand of K Q^T: chunk 2c + hi of row myq.
+  const FwdParams& p;
+  char* smem;
+  int tid, lane, w, hi, N, bh, qw0, myq, q0;
+  size_t base;
+  const uint16_t* K;
+  const uint16_t* V;
+  int goff[LOADS];       // element offset (row * D + chunk * 8) of this lane's direct loads
+  int grow[LOADS];       // tile row of each direct load
+  int kofs[DC];          // LDS byte offsets of the K operand reads (block 0, buffer 0)
+  int vofs[2][DB];       // LDS byte offsets of the V transpose reads (chunk 0, buffer 0)
   u32x4 qreg[DC];
-#pragma unroll
-  for (int c = 0; c < DC; ++c)
-    qreg[c] = (myq < N) ? ldg_b128(Q + (size_t)myq * D + (2 * c + hi) * 8) : u32x4{0, 0, 0, 0};
-
-  const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
-  const int n_tiles = (kv_end + BN - 1) / BN;
-
-  const int st_row = tid / CH, st_chunk = tid % CH;
-  u32x4 kst[PASSES], vst[PASSES];
-  auto load_tile = [&](int j) {
-#pragma unroll
-    for (int ps = 0; ps < PASSES; ++ps) {
-      const int key = j * BN + ps * ROWS_PER_PASS + st_row;
-      if (key < N) {
-        kst[ps] = ldg_b128(K + (size_t)key * D + st_chunk * 8);
-        vst[ps] = ldg_b128(V + (size_t)key * D + st_chunk * 8);
-      } else {
-        kst[ps] = u32x4{0, 0, 0, 0};
-        vst[ps] = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-    char* kl = smem + buf * 2 * TILE_BYTES;
-    char* vl = kl + TILE_BYTES;
-#pragma unroll
-    for (int ps = 0; ps < PASSES; ++ps) {
-      const int row = ps * ROWS_PER_PASS + st_row;
-      lds_write_b128(kl, swz<CH>(row, st_chunk), kst[ps]);
-      lds_write_b128(vl, swz<CH>(row, st_chunk), vst[ps]);
-    }
-  };
-
-  const float scale = p.scale;
-  const float cexp = SUNITS ? kLog2e : scale * kLog2e;
-  float M = kNegInf, M2 = kNegInf, m = kNegInf, lsum = 0.f;
-  bool flag = false;
   f32x16 oacc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+  float Mraw, M2raw, m, lsum;
+  bool flag;
 
-  // per-lane LDS offsets that do not depend on the tile
-  const int krow = sigma32(lane & 31);
-  const int g = lane >> 4, s = lane & 15;
-  const int tr_row = 8 * (g >> 1) + (s >> 2);   // + 16*kc + 4*half
-  const int tr_col = 16 * (g & 1) + 4 * (s & 3);  // + 32*db
+  __device__ FwdKernel(const FwdParams& p_, char* smem_) : p(p_), smem(smem_) {}
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int j = 0; j < n_tiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < n_tiles) load_tile(j + 1);
+  // Direct loads of key tile j (rows kv0 .. kv0 + 63) into buffer buf.
+  __device__ __forceinline__ void issue_tile(int j, int buf) {
     const int kv0 = j * BN;
-    const bool wave_active = (qw0 < N) && (!CAUSAL || kv0 <= qw0 + 31);
-    if (wave_active) {
-      const char* kl = smem + buf * 2 * TILE_BYTES;
-      const char* vl = kl + TILE_BYTES;
-      f32x16 sacc[KB];
+    char* kl = smem + buf * 2 * TILE;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        sacc[kb] = f32x16{};
-#pragma unroll
-        for (int c = 0; c < DC; ++c) {
-          const u32x4 a = lds_read_b128(kl, swz<CH>(kb * 32 + krow, 2 * c + hi));
-          sacc[kb] = mfma_bf16(a, qreg[c], sacc[kb]);
-        }
-      }
-      // scores: scale, mask, tile top-2 (or max)
-      const bool need_mask = (CAUSAL && kv0 + BN - 1 > qw0) || (kv0 + BN > N);
-      float t1 = kNegInf, t2 = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float sv = sacc[kb][r];
-          if (SUNITS) sv *= scale;
-          if (need_mask) {
-            const int key = kv0 + 32 * kb + 16 * (r >> 3) + 8 * hi + (r & 7);
-            if (key >= N || (CAUSAL && key > myq)) sv = kNegInf;
-          }
-          sacc[kb][r] = sv;
-          if (FLAGS) t2 = med3(t1, t2, sv);
-          t1 = fmaxf(t1, sv);
-        }
-      }
-      // combine the two lane halves that share a query
-      const float o1 = xchg32(t1);
-      if (FLAGS) {
-        const float o2 = xchg32(t2);
-        t2 = fmaxf(fminf(t1, o1), fmaxf(t2, o2));
-      }
-      t1 = fmaxf(t1, o1);
-      // running row maximum and second largest (multiset), tie flag, shift
-      if (FLAGS) M2 = fmaxf(fminf(M, t1), fmaxf(M2, t2));
-      M = fmaxf(M, t1);
-      if (FLAGS) flag = (M2 != kNegInf) && (M - M2 <= p.eps);
-      float m_new = M;
-      if (TIE && flag) m_new = (M > 0.f) ? p.beta * M : ((M < 0.f) ? 0.f : M);
-      float alpha;
-      float mb;
-      if (m_new == kNegInf) {  // no unmasked key seen yet for this row
-        alpha = 1.f;
-        mb = 0.f;
-      } else {
-        alpha = (m == kNegInf) ? 0.f : fast_exp2((m - m_new) * cexp);
-        mb = m_new * cexp;
-        m = m_new;
-      }
-      // probabilities, rounded to BF16 (or split hi + lo), row sums
-      uint32_t pk[KB][8];
-      uint32_t pl[KB][8];
-      float lt = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float pa = fast_exp2(fmaf(sacc[kb][2 * i], cexp, -mb));
-          const float pb = fast_exp2(fmaf(sacc[kb][2 * i + 1], cexp, -mb));
-          const uint32_t u = pack_bf16(pa, pb);
-          pk[kb][i] = u;
-          const float ha = bf16lo_to_f32(u), hb = bf16hi_to_f32(u);
-          if (HP) {
-            const uint32_t ul = pack_bf16(pa - ha, pb - hb);
-            pl[kb][i] = ul;
-            lt += (ha + bf16lo_to_f32(ul)) + (hb + bf16hi_to_f32(ul));
-          } else {
-            lt += ha + hb;
-          }
-        }
-      }
-      lsum = lsum * alpha + lt;
-      if (!__all(alpha == 1.f)) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      }
-      // O^T += V^T P-bar^T
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        const int kb = kc >> 1, o4 = 4 * (kc & 1);
-        const u32x4 bop = u32x4{pk[kb][o4], pk[kb][o4 + 1], pk[kb][o4 + 2], pk[kb][o4 + 3]};
-        u32x4 bop_lo;
-        if (HP) bop_lo = u32x4{pl[kb][o4], pl[kb][o4 + 1], pl[kb][o4 + 2], pl[kb][o4 + 3]};
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int row = 16 * kc + tr_row, col = 32 * db + tr_col;
-          const u32x2 a0 = lds_read_tr(vl, swz_elem<CH>(row, col));
-          const u32x2 a1 = lds_read_tr(vl, swz_elem<CH>(row + 4, col));
-          const u32x4 aop = u32x4{a0.x, a0.y, a1.x, a1.y};
-          oacc[db] = mfma_bf16(aop, bop, oacc[db]);
-          if (HP) oacc[db] = mfma_bf16(aop, bop_lo, oacc[db]);
-        }
-      }
+    for (int i = 0; i < LOADS; ++i) {
+      int off = kv0 * D + goff[i];
+      if (kv0 + BN > N && kv0 + grow[i] >= N) off = (N - 1) * D + (goff[i] - grow[i] * D);
+      char* dst = kl + (w * LOADS + i) * 1024;
+      g2lds_b128(K + off, dst);
+      g2lds_b128(V + off, dst + TILE);
     }
-    if (j + 1 < n_tiles) store_tile((j + 1) & 1);
-    __syncthreads();
   }
 
-  // epilogue: O = bf16(bf16(O-bar) / l)   or   O = O-bar / l (FP32 output)
-  const float ltot = lsum + xchg32(lsum);
-  if (myq < N) {
+  template <int BUF>
+  __device__ __forceinline__ void compute_tile(int j) {
+    const int kv0 = j * BN;
+    if (!(qw0 < N && (!CAUSAL || kv0 <= qw0 + 31))) return;  // no key of this tile is visible
+    const char* kl = smem + BUF * 2 * TILE;
+    const char* vl = kl + TILE;
+    f32x16 sacc[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      sacc[kb] = f32x16{};
+#pragma unroll
+      for (int c = 0; c < DC; ++c)
+        sacc[kb] = mfma_bf16(lds_read_b128(kl, kofs[c] + kb * 32 * ROWB), qreg[c], sacc[kb]);
+    }
+    // mask keys after the query (causal) and beyond the sequence, branch-free
+    const bool need_mask = (CAUSAL && kv0 + BN - 1 > qw0) || (kv0 + BN > N);
+    if (need_mask) {
+      const int lim = (CAUSAL ? min(myq, N - 1) : N - 1) - (kv0 + 8 * hi);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int off = 32 * kb + 16 * (r >> 3) + (r & 7);
+          sacc[kb][r] = off > lim ? kNegInf : sacc[kb][r];
+        }
+    }
+    // tile maximum (and second largest, as a multiset) of the raw dot products
+    float t1 = kNegInf, t2 = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if (FLAGS) t2 = med3(t1, t2, sacc[kb][r]);
+        t1 = fmaxf(t1, sacc[kb][r]);
+      }
+    // combine the two lane halves that share a query
+    float a1, b1;
+    pair32(t1, a1, b1);
+    if (FLAGS) {
+      float a2, b2;
+      pair32(t2, a2, b2);
+      t2 = fmaxf(fminf(a1, b1), fmaxf(a2, b2));
+      M2raw = fmaxf(fminf(Mraw, fmaxf(a1, b1)), fmaxf(M2raw, t2));
+    }
+    Mraw = fmaxf(Mraw, fmaxf(a1, b1));
+    // S-unit maximum, tie flag and shift (section 3.4.5)
+    const float Ms = Mraw * p.scale;
+    if (FLAGS) flag = (M2raw != kNegInf) && (Ms - M2raw * p.scale <= p.eps);
+    float m_new = Ms;
+    if (TIE && flag) m_new = (Ms > 0.f) ? p.beta * Ms : ((Ms < 0.f) ? 0.f : Ms);
+    float alpha = 1.f, mb = 0.f;
+    if (m_new != kNegInf) {
+      alpha = (m == kNegInf) ? 0.f : fast_exp2((m - m_new) * kLog2e);
+      mb = m_new * kLog2e;
+      m = m_new;
+    }
+    const float c1 = p.scale * kLog2e;
+    // P-bar = exp(S - m), rounded to BF16 (or split hi + lo), and its row sum
+    uint32_t pk[KB][8];
+    uint32_t pl[KB][8];
+    float lt = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float pa = fast_exp2(fmaf(sacc[kb][2 * i], c1, -mb));
+        const float pb = fast_exp2(fmaf(sacc[kb][2 * i + 1], c1, -mb));
+        const uint32_t u = pack_bf16(pa, pb);
+        pk[kb][i] = u;
+        lt = add_bf16_pair(u, lt);
+        if (HP) {
+          const uint32_t ul = pack_bf16(pa - bf16lo_to_f32(u), pb - bf16hi_to_f32(u));
+          pl[kb][i] = ul;
+          lt = add_bf16_pair(ul, lt);
+        }
+      }
+    lsum = fmaf(lsum, alpha, lt);
+    if (!__all(alpha == 1.f)) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+    // O^T += V^T P-bar^T
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      const int kb = kc >> 1, o4 = 4 * (kc & 1);
+      const u32x4 bop = u32x4{pk[kb][o4], pk[kb][o4 + 1], pk[kb][o4 + 2], pk[kb][o4 + 3]};
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const u32x2 a0 = lds_read_tr(vl, vofs[0][db] + kc * 16 * ROWB);
+        const u32x2 a1v = lds_read_tr(vl, vofs[1][db] + kc * 16 * ROWB);
+        const u32x4 aop = u32x4{a0.x, a0.y, a1v.x, a1v.y};
+        oacc[db] = mfma_bf16(aop, bop, oacc[db]);
+        if (HP) {
+          const u32x4 bl = u32x4{pl[kb][o4], pl[kb][o4 + 1], pl[kb][o4 + 2], pl[kb][o4 + 3]};
+          oacc[db] = mfma_bf16(aop, bl, oacc[db]);
+        }
+      }
+    }
+  }
+
+  template <int BUF>
+  __device__ __forceinline__ void step(int j, int n_tiles) {
+    if (j + 1 < n_tiles) issue_tile(j + 1, 1 - BUF);
+    compute_tile<BUF>(j);
+    wait_all_and_barrier();
+  }
+
+  __device__ __forceinline__ void run() {
+    tid = threadIdx.x;
+    lane = tid & 63;
+    w = tid >> 6;
+    hi = lane >> 5;
+    N = p.N;
+    int qb;
+    map_block(blockIdx.x, p.BH, p.n_qblocks, bh, qb);
+    base = (size_t)bh * N * D;
+    const uint16_t* Q = p.q + base;
+    K = p.k + base;
+    V = p.v + base;
+    q0 = qb * BM;
+    qw0 = q0 + 32 * w;
+    myq = qw0 + (lane & 31);
+
+#pragma unroll
+    for (int c = 0; c < DC; ++c)
+      qreg[c] = (myq < N) ? ldg_b128(Q + (size_t)myq * D + (2 * c + hi) * 8) : u32x4{0, 0, 0, 0};
+    // direct-load slots: wave w, load i covers LDS slots (w*LOADS + i)*64 + lane
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int slot = (w * LOADS + i) * 64 + lane;
+      const int row = slot / CH, pchunk = slot % CH;
+      grow[i] = row;
+      goff[i] = row * D + (pchunk ^ swz_pattern<CH>(row)) * 8;
+    }
+    const int krow = sigma32(lane & 31);
+#pragma unroll
+    for (int c = 0; c < DC; ++c) kofs[c] = swz<CH>(krow, 2 * c + hi);
+    const int g = lane >> 4, s = lane & 15;
+    const int tr_row = 8 * (g >> 1) + (s >> 2);
+    const int tr_col = 16 * (g & 1) + 4 * (s & 3);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) vofs[hh][db] = swz_elem<CH>(tr_row + 4 * hh, 32 * db + tr_col);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+    Mraw = kNegInf;
+    M2raw = kNegInf;
+    m = kNegInf;
+    lsum = 0.f;
+    flag = false;
+
+    const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
+    const int n_tiles = (kv_end + BN - 1) / BN;
+    issue_tile(0, 0);
+    wait_all_and_barrier();
+    for (int j = 0; j < n_tiles; j += 2) {
+      step<0>(j, n_tiles);
+      if (j + 1 < n_tiles) step<1>(j + 1, n_tiles);
+    }
+    epilogue();
+  }
+
+  // O = bf16(bf16(O-bar) / l)   or   O = O-bar / l (FP32 output)
+  __device__ __forceinline__ void epilogue() {
+    float la, lb;
+    pair32(lsum, la, lb);
+    const float ltot = la + lb;
+    if (myq >= N) return;
     const size_t orow = base + (size_t)myq * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -276,11 +303,17 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
       }
     }
     if (hi == 0) {
-      const float m_s = SUNITS ? m : m * scale;
-      p.lse[(size_t)bh * N + myq] = m_s + logf(ltot);
+      p.lse[(size_t)bh * N + myq] = m + logf(ltot);
       if (FLAGS && p.flags) p.flags[(size_t)bh * N + myq] = flag ? 1 : 0;
     }
   }
+};
+
+template <int D, int MODE, bool CAUSAL, bool FLAGS>
+__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
+  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * FwdKernel<D, MODE, CAUSAL, FLAGS>::TILE];
+  FwdKernel<D, MODE, CAUSAL, FLAGS> k(p, smem);
+  k.run();
 }
 
 template <int D, int MODE, bool CAUSAL, bool FLAGS>
@@ -305,12 +338,14 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
 
 template <int D, int MODE>
 hipError_t launch_m(const FwdArgs& a, hipStream_t stream) {
+  // the tie-aware shift needs the running second maximum; the plain modes
+  // track it only when the caller asks for the tie flags
   const bool flags = MODE == kTieAware || a.flags != nullptr;
   if (a.causal) {
-    if (MODE == kTieAware || flags) return launch_t<D, MODE, true, true>(a, stream);
+    if (flags) return launch_t<D, MODE, true, true>(a, stream);
     return launch_t<D, MODE, true, (MODE == kTieAware)>(a, stream);
   }
-  if (MODE == kTieAware || flags) return launch_t<D, MODE, false, true>(a, stream);
+  if (flags) return launch_t<D, MODE, false, true>(a, stream);
   return launch_t<D, MODE, false, (MODE == kTieAware)>(a, stream);
 }
 

@@ -61,6 +61,17 @@ __device__ __forceinline__ float med3(float a, float b, float c) { return __buil
 // Exchange with the lane 32 positions away (the other half of the wave).
 __device__ __forceinline__ float xchg32(float x) { return __shfl_xor(x, 32, 64); }
 
+// The value of x in this lane and in the lane 32 positions away, in an order
+// that depends on the lane (v_permlane32_swap): use only symmetric functions
+// of the pair (max, min, sum).
+__device__ __forceinline__ void pair32(float x, float& a, float& b) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const unsigned r0 = r[0], r1 = r[1];
+  a = __uint_as_float(r0);
+  b = __uint_as_float(r1);
+}
+
 // Two transpose reads of 4 x 16 blocks from a row-major LDS tile whose rows
 // are `row_bytes` long and whose 16-byte chunks are XOR-swizzled by row.
 __device__ __forceinline__ u32x2 lds_read_tr(const char* lds_base, int byte_off) {
@@ -106,5 +117,25 @@ __device__ __forceinline__ int swz_elem(int row, int col) {
 }
 
 __device__ __forceinline__ u32x4 ldg_b128(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Direct global -> LDS load of 16 bytes per lane (global_load_lds_dwordx4):
+// lane l's bytes land at lds_wave_base + 16 * l.  lds_wave_base must be the
+// same for the whole wave.  Completion is tracked by vmcnt.
+__device__ __forceinline__ void g2lds_b128(const void* gptr, char* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+
+// Wait for every outstanding memory operation of this wave (including direct
+// loads into LDS), then the workgroup barrier.
+__device__ __forceinline__ void wait_all_and_barrier() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+}
+
+// Sum of the two BF16 values packed in u, accumulated onto acc in FP32.
+__device__ __forceinline__ float add_bf16_pair(uint32_t u, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u),
+                                         __builtin_bit_cast(bf16x2, 0x3f803f80u), acc, false);
+}
 
 }  // namespace pfa

@@ -94,12 +94,12 @@ def test_small_shapes_fwd_bwd(gpu, name, wl, causal, mode):
         assert agree >= 0.9
 
 
-def _within_one_bf16_ulp(a, b):
-    """Elementwise within one BF16 ulp, plus a floor of 1e-5 of the tensor's
+def _within_one_bf16_ulp(a, b, ulps=1):
+    """Elementwise within `ulps` BF16 ulps, plus a floor of 1e-5 of the tensor's
     largest magnitude: a dQ element that is small because of cancellation
     carries FP32 summation noise that is large relative to itself."""
     floor = 1e-5 * max(np.abs(a).max(), np.abs(b).max())
-    return np.all(np.abs(a - b) <= 2.0 ** -7 * np.maximum(np.abs(a), np.abs(b)) + floor)
+    return np.all(np.abs(a - b) <= ulps * 2.0 ** -7 * np.maximum(np.abs(a), np.abs(b)) + floor)
 
 
 @pytest.mark.parametrize("mode", MODES)
@@ -128,8 +128,10 @@ def test_odd_symmetry_and_repeatability(gpu, mode):
         if mode == "fp32_out" and key == "o":
             assert st.max_rel_err(y, x) <= 1e-6
         else:
+            # O is rounded to BF16 twice (O-bar, then O-bar / l): a one-ulp
+            # flip of O-bar can show as up to two ulps of O
             assert np.mean(x != y) <= 1e-3, key
-            assert _within_one_bf16_ulp(x, y), key
+            assert _within_one_bf16_ulp(x, y, ulps=2 if key == "o" else 1), key
 
 
 def test_never_fired_rows_match_plain_bitwise(gpu):
