@@ -1,7 +1,7 @@
 """Benchmark: attention forward + backward throughput on one MI355X.
 
-One step = attn_fwd + the three backward stages (attn_bwd_prep, attn_bwd_main,
-attn_bwd_finish) over one batch of synthetic inputs already resident in HBM:
+One step = attn_fwd + the three backward kernels (attn_bwd_prep, attn_bwd_dkdv,
+attn_bwd_dq) over one batch of synthetic inputs already resident in HBM:
 the long-context workload B=1, H=16, N=8192, d=128, causal (the headline
 throughput configuration).  Throughput counts the algorithmic FLOPs
 7 * B * H * N^2 * d (forward: S = QK^T and P-bar V; backward: the S recompute,
@@ -93,13 +93,14 @@ def run_mode(torch, pfa, inp, wl, mode, steps, warmup):
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
     ws = torch.empty(pfa.attn_bwd_workspace_bytes(B, H, N, d, mode), device=dev, dtype=torch.uint8)
     stream = torch.cuda.current_stream()
-    stages = ("fwd", "bwd_prep", "bwd_main", "bwd_finish")
+    stages = ("fwd", "bwd_prep", "bwd_dkdv", "bwd_dq")
     calls = {
         "fwd": lambda: pfa.attn_fwd(q, k, v, o, lse, flags, causal=True, mode=mode, stream=stream),
         "bwd_prep": lambda: pfa.attn_bwd_prep(o, do, ws, mode=mode, stream=stream),
-        "bwd_main": lambda: pfa.attn_bwd_main(q, k, v, do, lse, dk, dv, ws, causal=True, mode=mode,
+        "bwd_dkdv": lambda: pfa.attn_bwd_dkdv(q, k, v, do, lse, dk, dv, ws, causal=True, mode=mode,
                                               stream=stream),
-        "bwd_finish": lambda: pfa.attn_bwd_finish(dq, ws, stream=stream),
+        "bwd_dq": lambda: pfa.attn_bwd_dq(q, k, v, do, lse, dq, ws, causal=True, mode=mode,
+                                          stream=stream),
     }
     for _ in range(warmup):
         for s in stages:
@@ -163,14 +164,17 @@ def main():
     inp = generate(wl)
     flops = wl.flops()
     # forward: two products (S = QK^T, P-bar V) of 2 N^2 d each per head, halved by the mask
-    fwd_flops = 4 * wl.b * wl.h * wl.n * wl.n * wl.d // (2 if wl.causal else 1)
+    unit = wl.b * wl.h * wl.n * wl.n * wl.d // (2 if wl.causal else 1)  # N^2 d per head, masked
+    fwd_flops = 4 * unit   # S = QK^T and P-bar V
     bwd_flops = flops - fwd_flops
+    # algorithmic work of each kernel: dK/dV kernel = S recompute, dP, dV, dK (8 unit);
+    # dQ kernel = dQ alone (2 unit) -- it recomputes S and dP, which count once, above
+    kern_flops = {"fwd": fwd_flops, "bwd_dkdv": 8 * unit, "bwd_dq": 2 * unit}
 
     ms, phases, ties = run_mode(torch, pfa, inp, wl, args.mode, args.steps, args.warmup)
     value = flops / (ms * 1e-3) / 1e12
 
-    kern_flops = {"fwd": fwd_flops, "bwd_main": bwd_flops}
-    kname = {"fwd": "fwd_kernel", "bwd_main": "bwd_main_kernel"}
+    kname = {"fwd": "fwd_kernel", "bwd_dkdv": "bwd_dkdv_kernel", "bwd_dq": "bwd_dq_kernel"}
     dom = max(kern_flops, key=lambda s: phases[s])
     achieved = kern_flops[dom] / (phases[dom] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,

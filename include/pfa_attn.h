@@ -97,8 +97,10 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int32_t* tie_flags, int B, int H, int N, int d, int causal, float scale,
              int mode, const pfa_tie_opts* opts, void* stream);
 
-/* Bytes of device workspace attn_bwd needs: an FP32 dQ accumulator and the
- * FP32 delta row vector, each 256-byte aligned.  0 on invalid sizes. */
+/* Bytes of device workspace the backward needs: room for the FP32 delta row
+ * vector [B,H,N] (used when the caller passes no delta buffer) and, in
+ * PFA_FP32_OUT, a BF16 copy of dO for the MFMA operands; 256-byte aligned
+ * parts.  0 on invalid sizes. */
 size_t attn_bwd_workspace_bytes(int B, int H, int N, int d, int mode);
 
 /*
@@ -114,9 +116,8 @@ size_t attn_bwd_workspace_bytes(int B, int H, int N, int d, int mode);
  *   dq, dk, dv      out  BF16 [B,H,N,d]
  *   delta           out  FP32 [B,H,N] or NULL: delta as used, for diagnostics
  *   workspace       in   device memory of at least attn_bwd_workspace_bytes;
- *                        contents on entry are ignored (the library clears what
- *                        it needs with a kernel, so the call can be captured in
- *                        a HIP graph)
+ *                        contents on entry are ignored
+ * No atomics are used: dQ, dK and dV are bitwise reproducible.
  */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
              const float* lse, void* dq, void* dk, void* dv, float* delta,
@@ -124,29 +125,32 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              int causal, float scale, int mode, void* stream);
 
 /*
- * The backward in its three stages, for callers that schedule or time them
+ * The backward in its three kernels, for callers that schedule or time them
  * separately.  attn_bwd runs exactly these three on one stream; running them
- * in order on one stream with the same workspace gives the same result.
+ * in this order on one stream gives the same result.
  *
  * Stage 1, attn_bwd_prep: delta = rowsum(dO o O) in FP32 -- the term the
  * pages single out as computed apart in the backward (section 3.4.2) -- into
- * `delta` (or into the workspace when delta is NULL), and clears the FP32 dQ
- * accumulator in the workspace.  o, dout: BF16 (FP32 in PFA_FP32_OUT).
+ * `delta` (or into the workspace when delta is NULL).  o, dout: BF16 (FP32 in
+ * PFA_FP32_OUT).
  */
 int attn_bwd_prep(const void* o, const void* dout, float* delta, void* workspace,
                   size_t workspace_bytes, int B, int H, int N, int d, int mode, void* stream);
 
-/* Stage 2, attn_bwd_main: P = exp(S - LSE), dP = dO V^T,
- * dS = P o (dP - delta); writes dV = P^T dO and dK = scale dS^T Q (BF16) and
- * adds dS K into the FP32 dQ accumulator (sections 3.4.2, 3.4.3).  delta: the
- * vector stage 1 wrote (NULL = the workspace copy). */
-int attn_bwd_main(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+/* Stage 2, attn_bwd_dkdv: P = exp(S - LSE), dP = dO V^T, dS = P o (dP - delta);
+ * writes dV = P^T dO and dK = scale dS^T Q (BF16) (sections 3.4.2, 3.4.3).
+ * delta: the vector stage 1 wrote (NULL = the workspace copy).  In
+ * PFA_FP32_OUT stages 2 and 3 take dO from the BF16 copy stage 1 left in the
+ * workspace, so they need the same workspace, after stage 1. */
+int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                   const float* delta, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                   int B, int H, int N, int d, int causal, float scale, int mode, void* stream);
 
-/* Stage 3, attn_bwd_finish: dQ = bf16(scale * accumulator). */
-int attn_bwd_finish(void* dq, const void* workspace, size_t workspace_bytes, int B, int H, int N,
-                    int d, float scale, void* stream);
+/* Stage 3, attn_bwd_dq: recomputes P and dS per query block and writes
+ * dQ = scale dS K (BF16) (section 3.4.3).  delta as in stage 2. */
+int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                const float* delta, void* dq, void* workspace, size_t workspace_bytes, int B, int H,
+                int N, int d, int causal, float scale, int mode, void* stream);
 
 /* Static text for a status code. */
 const char* attn_strerror(int status);

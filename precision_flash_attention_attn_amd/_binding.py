@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_PKG, "_lib", "libpfa_attn.so")
 
 MODES = {"bf16_out": 0, "fp32_out": 1, "tie_aware_softmax": 2}
 PFA_OK, PFA_ERR_INVALID, PFA_ERR_UNSUPPORTED, PFA_ERR_HIP = 0, -1, -2, -3
-EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_prep", "attn_bwd_main", "attn_bwd_finish",
+EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_prep", "attn_bwd_dkdv", "attn_bwd_dq",
             "attn_bwd_workspace_bytes", "attn_strerror", "attn_version")
 
 
@@ -51,11 +51,12 @@ def lib() -> ctypes.CDLL:
         L.attn_bwd.restype = i
         L.attn_bwd_prep.argtypes = [vp, vp, vp, vp, ctypes.c_size_t, i, i, i, i, i, vp]
         L.attn_bwd_prep.restype = i
-        L.attn_bwd_main.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+        L.attn_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                     i, i, i, i, i, f, i, vp]
-        L.attn_bwd_main.restype = i
-        L.attn_bwd_finish.argtypes = [vp, vp, ctypes.c_size_t, i, i, i, i, f, vp]
-        L.attn_bwd_finish.restype = i
+        L.attn_bwd_dkdv.restype = i
+        L.attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                  i, i, i, i, i, f, i, vp]
+        L.attn_bwd_dq.restype = i
         L.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
         L.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.attn_strerror.argtypes = [i]
@@ -152,7 +153,7 @@ def _ws(workspace):
 
 
 def attn_bwd_prep(o, dout, workspace, delta=None, mode="bf16_out", stream=None):
-    """Backward stage 1: delta = rowsum(dO o O), clear the dQ accumulator."""
+    """Backward stage 1: delta = rowsum(dO o O)."""
     B, H, N, d = o.shape
     mid = _mode_id(mode)
     io = torch.float32 if mid == 1 else torch.bfloat16
@@ -165,31 +166,41 @@ def attn_bwd_prep(o, dout, workspace, delta=None, mode="bf16_out", stream=None):
                                _stream(stream)))
 
 
-def attn_bwd_main(q, k, v, dout, lse, dk, dv, workspace, delta=None, causal=True, scale=None,
-                  mode="bf16_out", stream=None):
-    """Backward stage 2: dK, dV and the FP32 dQ accumulation."""
+def _stage_args(q, k, v, dout, lse, delta, mode):
     B, H, N, d = q.shape
     mid = _mode_id(mode)
-    for name, t in (("q", q), ("k", k), ("v", v), ("dk", dk), ("dv", dv)):
+    for name, t in (("q", q), ("k", k), ("v", v)):
         _expect(t, name, torch.bfloat16, (B, H, N, d))
     _expect(dout, "dout", torch.float32 if mid == 1 else torch.bfloat16, (B, H, N, d))
     _expect(lse, "lse", torch.float32, (B, H, N))
     if delta is not None:
         _expect(delta, "delta", torch.float32, (B, H, N))
+    return B, H, N, d, mid
+
+
+def attn_bwd_dkdv(q, k, v, dout, lse, dk, dv, workspace, delta=None, causal=True, scale=None,
+                  mode="bf16_out", stream=None):
+    """Backward stage 2: dK and dV."""
+    B, H, N, d, mid = _stage_args(q, k, v, dout, lse, delta, mode)
+    _expect(dk, "dk", torch.bfloat16, (B, H, N, d))
+    _expect(dv, "dv", torch.bfloat16, (B, H, N, d))
     scale = 1.0 / d ** 0.5 if scale is None else float(scale)
     wp, wn = _ws(workspace)
-    _check(lib().attn_bwd_main(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(delta),
+    _check(lib().attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(delta),
                                _ptr(dk), _ptr(dv), wp, wn, B, H, N, d, int(bool(causal)), scale, mid,
                                _stream(stream)))
 
 
-def attn_bwd_finish(dq, workspace, scale=None, stream=None):
-    """Backward stage 3: dQ = bf16(scale * accumulator)."""
-    B, H, N, d = dq.shape
+def attn_bwd_dq(q, k, v, dout, lse, dq, workspace, delta=None, causal=True, scale=None,
+                mode="bf16_out", stream=None):
+    """Backward stage 3: dQ."""
+    B, H, N, d, mid = _stage_args(q, k, v, dout, lse, delta, mode)
     _expect(dq, "dq", torch.bfloat16, (B, H, N, d))
     scale = 1.0 / d ** 0.5 if scale is None else float(scale)
     wp, wn = _ws(workspace)
-    _check(lib().attn_bwd_finish(_ptr(dq), wp, wn, B, H, N, d, scale, _stream(stream)))
+    _check(lib().attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(delta),
+                             _ptr(dq), wp, wn, B, H, N, d, int(bool(causal)), scale, mid,
+                             _stream(stream)))
 
 
 # ---- conveniences that allocate with torch and call the entry points above ----

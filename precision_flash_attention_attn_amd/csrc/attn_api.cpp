@@ -78,7 +78,7 @@ size_t attn_bwd_workspace_bytes(int B, int H, int N, int d, int mode) {
   if (check_sizes(B, H, N, d) != PFA_OK) return 0;
   if (mode != PFA_BF16_OUT && mode != PFA_FP32_OUT && mode != PFA_TIE_AWARE_SOFTMAX) return 0;
   const size_t rows = size_t(B) * H * N;
-  return pfa::bwd_dq_acc_bytes(rows, d) + pfa::bwd_delta_bytes(rows);
+  return pfa::bwd_delta_bytes(rows) + pfa::bwd_dout16_bytes(rows, d, mode);
 }
 
 namespace {
@@ -92,11 +92,12 @@ int bwd_args(pfa::BwdArgs& a, void* workspace, size_t workspace_bytes, float* de
   if (delta && !aligned4(delta)) return PFA_ERR_INVALID;
   const size_t need = attn_bwd_workspace_bytes(B, H, N, d, mode);
   if (need == 0 || workspace_bytes < need) return PFA_ERR_INVALID;
-  const size_t rows = size_t(B) * H * N;
-  char* ws = static_cast<char*>(workspace);
   a = pfa::BwdArgs{};
-  a.dq_acc = reinterpret_cast<float*>(ws);
-  a.delta = delta ? delta : reinterpret_cast<float*>(ws + pfa::bwd_dq_acc_bytes(rows, d));
+  const size_t rows = size_t(B) * H * N;
+  a.delta = delta ? delta : static_cast<float*>(workspace);
+  a.dout16 = mode == PFA_FP32_OUT
+                 ? reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + pfa::bwd_delta_bytes(rows))
+                 : nullptr;
   a.B = B;
   a.H = H;
   a.N = N;
@@ -124,7 +125,7 @@ int attn_bwd_prep(const void* o, const void* dout, float* delta, void* workspace
   return status_of(pfa::launch_bwd_prep(a, static_cast<hipStream_t>(stream)));
 }
 
-int attn_bwd_main(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                   const float* delta, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                   int B, int H, int N, int d, int causal, float scale, int mode, void* stream) {
   pfa::BwdArgs a;
@@ -140,18 +141,25 @@ int attn_bwd_main(const void* q, const void* k, const void* v, const void* dout,
   a.lse = lse;
   a.dk = dk;
   a.dv = dv;
-  return status_of(pfa::launch_bwd_main(a, static_cast<hipStream_t>(stream)));
+  return status_of(pfa::launch_bwd_dkdv(a, static_cast<hipStream_t>(stream)));
 }
 
-int attn_bwd_finish(void* dq, const void* workspace, size_t workspace_bytes, int B, int H, int N,
-                    int d, float scale, void* stream) {
+int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                const float* delta, void* dq, void* workspace, size_t workspace_bytes, int B, int H,
+                int N, int d, int causal, float scale, int mode, void* stream) {
   pfa::BwdArgs a;
-  const int st = bwd_args(a, const_cast<void*>(workspace), workspace_bytes, nullptr, B, H, N, d, 1,
-                          scale, PFA_BF16_OUT);
+  const int st = bwd_args(a, workspace, workspace_bytes, const_cast<float*>(delta), B, H, N, d,
+                          causal, scale, mode);
   if (st != PFA_OK) return st;
-  if (!ok16(dq)) return PFA_ERR_INVALID;
+  if (!ok16(q) || !ok16(k) || !ok16(v) || !ok16(dout) || !ok16(dq)) return PFA_ERR_INVALID;
+  if (!lse || !aligned4(lse)) return PFA_ERR_INVALID;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  a.lse = lse;
   a.dq = dq;
-  return status_of(pfa::launch_bwd_finish(a, static_cast<hipStream_t>(stream)));
+  return status_of(pfa::launch_bwd_dq(a, static_cast<hipStream_t>(stream)));
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -176,8 +184,8 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   a.dv = dv;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = pfa::launch_bwd_prep(a, s);
-  if (e == hipSuccess) e = pfa::launch_bwd_main(a, s);
-  if (e == hipSuccess) e = pfa::launch_bwd_finish(a, s);
+  if (e == hipSuccess) e = pfa::launch_bwd_dkdv(a, s);
+  if (e == hipSuccess) e = pfa::launch_bwd_dq(a, s);
   return status_of(e);
 }
 

@@ -33,23 +33,26 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* delta;     // where delta is written (caller's buffer or workspace)
-  float* dq_acc;    // FP32 dQ accumulator in the workspace
+  uint16_t* dout16; // BF16 copy of an FP32 dO in the workspace (FP32-output mode)
   int B, H, N, d;
   int causal;
   int mode;
   float scale;
 };
 
-// Workspace layout of the backward: [dQ accumulator | delta], 256-byte aligned parts.
+// Workspace of the backward: the FP32 delta row vector, then (FP32-output
+// mode only) a BF16 copy of dO; 256-byte aligned parts.
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
-inline size_t bwd_dq_acc_bytes(size_t rows, int d) { return align256(rows * (size_t)d * 4); }
 inline size_t bwd_delta_bytes(size_t rows) { return align256(rows * 4); }
+inline size_t bwd_dout16_bytes(size_t rows, int d, int mode) {
+  return mode == kFp32Out ? align256(rows * (size_t)d * 2) : 0;
+}
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
-// The backward in three stages on one stream: delta and the cleared dQ
-// accumulator; dK, dV and the dQ accumulation; dQ conversion to BF16.
+// The backward in three kernels on one stream: delta = rowsum(dO o O); dK and
+// dV; dQ.
 hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t stream);
-hipError_t launch_bwd_main(const BwdArgs& a, hipStream_t stream);
-hipError_t launch_bwd_finish(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 
 }  // namespace pfa

@@ -46,10 +46,10 @@ def test_strerror(L):
 
 
 def test_workspace_bytes(L):
-    n = L.attn_bwd_workspace_bytes(1, 16, 8192, 128, 0)
     rows = 16 * 8192
-    assert n == rows * 128 * 4 + rows * 4
-    assert L.attn_bwd_workspace_bytes(1, 1, 1, 64, 0) == 512          # two 256-byte-aligned parts
+    assert L.attn_bwd_workspace_bytes(1, 16, 8192, 128, 0) == rows * 4   # the delta vector
+    assert L.attn_bwd_workspace_bytes(1, 16, 8192, 128, 1) == rows * 4 + rows * 128 * 2  # + BF16 dO
+    assert L.attn_bwd_workspace_bytes(1, 1, 1, 64, 0) == 256             # 256-byte aligned
     assert L.attn_bwd_workspace_bytes(1, 1, 1, 96, 0) == 0
     assert L.attn_bwd_workspace_bytes(0, 1, 1, 64, 0) == 0
     assert L.attn_bwd_workspace_bytes(1, 1, 1, 64, 7) == 0
@@ -126,18 +126,16 @@ def test_backward_stages_reject_invalid_arguments(L):
     assert L.attn_bwd_prep(FAKE, FAKE, None, FAKE, need, 1, 1, 128, 32, 0, None) == uns
     assert L.attn_bwd_prep(FAKE, FAKE, FAKE + 2, FAKE, need, 1, 1, 128, 64, 0, None) == inv
     args = [FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, need, 1, 1, 128, 64, 1, 0.125, 0, None]
-    bad = list(args)
-    bad[4] = None                                    # lse
-    assert L.attn_bwd_main(*bad) == inv
-    bad = list(args)
-    bad[7] = FAKE + 8                                # dv misaligned
-    assert L.attn_bwd_main(*bad) == inv
-    bad = list(args)
-    bad[15] = float("nan")                           # scale
-    assert L.attn_bwd_main(*bad) == inv
-    bad = list(args)
-    bad[16] = 9                                      # mode
-    assert L.attn_bwd_main(*bad) == inv
-    assert L.attn_bwd_finish(None, FAKE, need, 1, 1, 128, 64, 0.125, None) == inv
-    assert L.attn_bwd_finish(FAKE, FAKE, need, 1, 1, 128, 64, 0.0, None) == inv
-    assert L.attn_bwd_finish(FAKE, FAKE, need - 1, 1, 1, 128, 64, 0.125, None) == inv
+    for fn in (L.attn_bwd_dkdv,):
+        for pos, val in ((4, None), (7, FAKE + 8), (15, float("nan")), (16, 9), (9, need - 1)):
+            bad = list(args)
+            bad[pos] = val
+            assert fn(*bad) == inv, pos
+    dq_args = [FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, need, 1, 1, 128, 64, 1, 0.125, 0, None]
+    for pos, val in ((0, None), (6, FAKE + 4), (14, 0.0), (15, 3), (8, 0)):
+        bad = list(dq_args)
+        bad[pos] = val
+        assert L.attn_bwd_dq(*bad) == inv, pos
+    bad = list(dq_args)
+    bad[12] = 48
+    assert L.attn_bwd_dq(*bad) == uns

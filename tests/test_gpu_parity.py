@@ -104,8 +104,7 @@ def _within_one_bf16_ulp(a, b, ulps=1):
 
 @pytest.mark.parametrize("mode", MODES)
 def test_odd_symmetry_and_repeatability(gpu, mode):
-    """Repeatability: the forward, dK and dV are bitwise repeatable; dQ sums FP32
-    atomics in a varying order, so it may differ by one BF16 ulp.
+    """Repeatability: every output is bitwise repeatable (no atomics).
     Odd symmetry in V: every step the oracle models is odd, and the oracle is
     bitwise odd.  The MFMA's internal accumulation is not exactly sign-symmetric
     on this hardware, so on the GPU a few BF16 outputs (about 1 in 10^5) may
@@ -114,9 +113,8 @@ def test_odd_symmetry_and_repeatability(gpu, mode):
     inp = generate(wl)
     a = gpu.run(inp, mode)
     b = gpu.run(inp, mode)
-    for key in ("o", "lse", "flags", "dk", "dv", "delta"):
+    for key in ("o", "lse", "flags", "dq", "dk", "dv", "delta"):
         assert np.array_equal(a[key], b[key]), key
-    assert _within_one_bf16_ulp(a["dq"], b["dq"])
     neg = generate(wl)
     neg.v = -neg.v
     c = gpu.run(neg, mode)
@@ -240,8 +238,8 @@ def test_full_size_configs(gpu, wid, modes, slices):
 
 @pytest.mark.parametrize("mode", MODES)
 def test_backward_stages_equal_one_call(gpu, mode):
-    """attn_bwd_prep + attn_bwd_main + attn_bwd_finish on one stream give what
-    attn_bwd gives (dK, dV, delta bitwise; dQ up to the atomic summation order)."""
+    """attn_bwd_prep + attn_bwd_dkdv + attn_bwd_dq on one stream give bit for
+    bit what attn_bwd gives (no atomics anywhere)."""
     import precision_flash_attention_attn_amd as pfa
     wl = Workload(89, "stages", 2, 2, 260, 128, tie_frac=0.05, tie_q_scale=8.0)
     inp = generate(wl)
@@ -250,14 +248,12 @@ def test_backward_stages_equal_one_call(gpu, mode):
     o, lse, _ = pfa.forward(q, k, v, mode=mode)
     dq1, dk1, dv1, de1 = pfa.backward(q, k, v, o, do, lse, mode=mode, want_delta=True)
     ws = torch.full((pfa.attn_bwd_workspace_bytes(*q.shape, mode),), 0x7F, device=q.device,
-                    dtype=torch.uint8)  # garbage on entry: stage 1 must clear what it needs
+                    dtype=torch.uint8)  # garbage on entry
     dq2, dk2, dv2 = (torch.empty_like(q) for _ in range(3))
-    de2 = torch.empty_like(lse)
-    pfa.attn_bwd_prep(o, do, ws, delta=de2, mode=mode)
-    pfa.attn_bwd_main(q, k, v, do, lse, dk2, dv2, ws, delta=de2, mode=mode)
-    pfa.attn_bwd_finish(dq2, ws)
+    pfa.attn_bwd_prep(o, do, ws, mode=mode)
+    pfa.attn_bwd_dkdv(q, k, v, do, lse, dk2, dv2, ws, mode=mode)
+    pfa.attn_bwd_dq(q, k, v, do, lse, dq2, ws, mode=mode)
     torch.cuda.synchronize()
     h = gpu.host
-    assert np.array_equal(h(dk1), h(dk2)) and np.array_equal(h(dv1), h(dv2))
-    assert np.array_equal(h(de1), h(de2))
-    assert _within_one_bf16_ulp(h(dq1), h(dq2))
+    for a, b in ((dq1, dq2), (dk1, dk2), (dv1, dv2)):
+        assert np.array_equal(h(a), h(b))
