@@ -30,7 +30,7 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense BF16 MFMA: 256 CU x 2.4 GHz x 4096 FL
 HBM_PEAK_GBS = 8000.0
 METRIC = "attention fwd+bwd TFLOP/s and % of bf16 MFMA peak; mean signed O error on tied rows"
 CSRC = os.path.join(ROOT, "precision_flash_attention_attn_amd", "csrc")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
 def source_hash() -> str:

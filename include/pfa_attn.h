@@ -15,9 +15,10 @@
  *                           paper-graph-ui, section 3.4.4).
  *   PFA_FP32_OUT            remedy 1: O is kept in FP32 and P-bar enters the
  *                           product at high precision (a two-term BF16
- *                           expansion hi + lo), section 3.4.2 "compute O in high
- *                           precision" and section 3.4.4 "computing only
- *                           O-bar = P-bar V in FP32".  dO is FP32 in this mode.
+ *                           expansion hi + lo).  Section 3.4.2 reports that an
+ *                           FP32 O stabilises training and section 3.4.4 that
+ *                           an FP32 P-bar V product alone suffices.  dO is
+ *                           FP32 in this mode.
  *   PFA_TIE_AWARE_SOFTMAX   remedy 2: the repeated-maximum-aware safe softmax of
  *                           section 3.4.5.  With rm the row maximum and
  *                           rs = #{t : rm - S_t <= eps}, the shift is beta*rm

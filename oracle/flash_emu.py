@@ -25,15 +25,15 @@ causal attention), starting from M = M2 = m = -inf, l = 0, Obar = 0:
  5. p_t = exp(fp32(S_t - m_new)) in FP32.
  6. P-bar_t = bf16(p_t) in the BF16 modes.  In the FP32-output mode the
     product uses the high-precision P-bar: hi + lo with hi = bf16(p),
-    lo = bf16(p - hi)  (section 3.4.4, "computing only O-bar = P-bar V in FP32
-    is sufficient to stabilize training").
+    lo = bf16(p - hi)  (section 3.4.4 reports that an FP32 P-bar V product
+    alone is enough to stabilise training).
  7. l = fp32(alpha * l + sum_t P-bar_t) and Obar = fp32(alpha * Obar +
     sum_t P-bar_t v_t): FP32 accumulation, each tile's sum formed exactly and
     rounded once.  l sums the same P-bar that multiplies V, as in the pages'
     O = Obar / rowsum(P-bar).
- 8. Epilogue.  BF16 modes: Obar is rounded to BF16 once ("compute the dot
-    product in FP32, then round the final result to BF16", section 3.4.4) and
-    O = bf16(fp32(bf16(Obar) / l)).  FP32-output mode: O = fp32(Obar / l).
+ 8. Epilogue.  BF16 modes: Obar is rounded to BF16 once (section 3.4.4 defines
+    the low-precision product as an FP32 dot product whose final result is
+    rounded to BF16) and O = bf16(fp32(bf16(Obar) / l)).  FP32-output mode: O = fp32(Obar / l).
     LSE = fp32(m + log l).  The output flag is the flag after the last tile.
 
 Readings where the pages leave a step open (listed with reasons in the design
