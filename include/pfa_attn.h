@@ -37,15 +37,16 @@
  * stream (a hipStream_t; NULL is the default stream).  Calls are asynchronous:
  * a device fault surfaces at the caller's next synchronisation.
  *
- * Supported: d in {64, 128}; any N >= 1 (ragged tails are masked); B, H >= 1;
- * B*H*N*d < 2^40.
+ * Supported: d in {64, 128}; any N >= 1 (ragged tails are masked) with
+ * N*d < 2^29 (byte offsets inside one (batch, head) slice stay 32-bit);
+ * B, H >= 1; B*H*N*d < 2^40.
  *
  * Errors: arguments are checked before anything is launched; a failed check
  * returns a negative status and writes nothing.  PFA_ERR_INVALID for a NULL
  * required pointer, misaligned pointer, non-positive or oversized B/H/N,
  * non-finite or non-positive scale, unknown mode, beta <= 1 or non-finite,
  * eps < 0 or non-finite, a too small workspace.  PFA_ERR_UNSUPPORTED for
- * d not in {64, 128}.  PFA_ERR_HIP if a launch fails.
+ * d not in {64, 128} or N*d >= 2^29.  PFA_ERR_HIP if a launch fails.
  *
  * Numerical note (tie-aware mode): when (beta - 1) * rm exceeds the FP32
  * exponent range (about 87) on a tied row, every P-bar underflows, the row sum

@@ -21,6 +21,8 @@ int check_sizes(int B, int H, int N, int d) {
   // grid sizes: (B*H) * ceil(N/128) workgroups must fit a 31-bit grid
   if (bh * ((int64_t(N) + 127) / 128) >= (int64_t(1) << 31)) return PFA_ERR_INVALID;
   if (d != 64 && d != 128) return PFA_ERR_UNSUPPORTED;
+  // tiles are staged with 32-bit byte offsets inside one (batch, head) slice
+  if (int64_t(N) * d >= (int64_t(1) << 29)) return PFA_ERR_UNSUPPORTED;
   return PFA_OK;
 }
 

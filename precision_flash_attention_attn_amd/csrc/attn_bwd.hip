@@ -111,17 +111,18 @@ struct DkdvKernel {
   static constexpr int ROWB = CH * 16;
   static constexpr int QT = BQ * D * 2;              // bytes of a Q (or dO) tile
   static constexpr int KBLK = BKV * D * 2;           // bytes of the key block
-  static constexpr int BUFB = 2 * QT + 2 * BQ * 4;   // Q, dO, LSE, delta
+  static constexpr int STAT = 2 * BQ * 4;            // LSE and delta of a query tile
+  static constexpr int BUFB = STAT + 2 * QT;         // one tile buffer: LSE, delta, Q, dO
+  static constexpr int KOFF = 2 * BUFB;              // the key block follows the two buffers
   static constexpr int LOADS = QT / (NT * 16);       // direct loads per thread per tile
   static constexpr int KLOADS = KBLK / (NT * 16);    // direct loads per thread for the key block
 
   const DkdvParams& p;
-  char* smem;   // [key block | buffer 0 | buffer 1]
-  int tid, lane, w, hi, kb, qh, N, bh, kv0, kw0, mykey;
+  char* smem;   // [buffer 0 | buffer 1 | key block]
+  int tid, lane, w, hi, kb, qh, N, bh, kv0, kw0, mykey, qt_begin;
   size_t base;
-  const uint16_t* Q;
-  const uint16_t* DO;
-  int goff[LOADS], grow[LOADS];
+  __amdgpu_buffer_rsrc_t qrs, dors, lrs, drs;   // this slice of Q, dO, LSE, delta
+  int voff[LOADS];   // byte offset in a tile of this lane's direct loads
   int aofs[DC];      // LDS offsets of the Q / dO operand reads (this wave's query half)
   int kofs[DC];      // LDS offsets of the K operand reads (this wave's keys)
   int tofs[2][DB];   // LDS offsets of the transpose reads
@@ -130,33 +131,49 @@ struct DkdvKernel {
 
   __device__ DkdvKernel(const DkdvParams& p_, char* smem_) : p(p_), smem(smem_) {}
 
-  // Direct loads of query tile qt0 (Q, dO, LSE, delta) into buffer buf.
+  // Direct loads of the query tile at qt0 (Q, dO, LSE, delta) into buffer buf.
   __device__ __forceinline__ void issue_tile(int qt0, int buf) {
-    char* bl = smem + KBLK + buf * BUFB;
+    char* bl = smem + buf * BUFB;
+    if (qt0 + BQ <= N) {
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      int off = qt0 * D + goff[i];
-      if (qt0 + BQ > N && qt0 + grow[i] >= N) off = (N - 1) * D + (goff[i] - grow[i] * D);
-      char* dst = bl + (w * LOADS + i) * 1024;
-      g2lds_b128(Q + off, dst);
-      g2lds_b128(DO + off, dst + QT);
-    }
-    if (w == 0 || w == 1) {
-      const int r = min(qt0 + lane, N - 1);
-      const float* src = (w == 0 ? p.lse : p.delta) + (size_t)bh * N + r;
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(bl + 2 * QT + w * BQ * 4),
-                                       4, 0, 0);
+      for (int i = 0; i < LOADS; ++i) {
+        char* dst = bl + STAT + (w * LOADS + i) * 1024;
+        buf2lds_b128(qrs, voff[i], qt0 * D * 2, dst);
+        buf2lds_b128(dors, voff[i], qt0 * D * 2, dst + QT);
+      }
+      if (w < 2)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(w == 0 ? lrs : drs,
+                                                 (__attribute__((address_space(3))) void*)(bl + w * BQ * 4),
+                                                 4, lane * 4, qt0 * 4, 0, 0);
+    } else {
+      // ragged last tile: rows past the end repeat row N-1 (masked later)
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int row = ((w * LOADS + i) * 64 + lane) / CH;
+        const int off = voff[i] + (min(qt0 + row, N - 1) - row) * D * 2;
+        char* dst = bl + STAT + (w * LOADS + i) * 1024;
+        buf2lds_b128(qrs, off, 0, dst);
+        buf2lds_b128(dors, off, 0, dst + QT);
+      }
+      if (w < 2)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(w == 0 ? lrs : drs,
+                                                 (__attribute__((address_space(3))) void*)(bl + w * BQ * 4),
+                                                 4, min(qt0 + lane, N - 1) * 4, 0, 0, 0);
     }
   }
 
-  __device__ __forceinline__ void compute_tile(int qt0, int buf) {
-    const char* kl = smem;
-    const char* ql = smem + KBLK + buf * BUFB;
-    const char* dl = ql + QT;
-    const float* sl = reinterpret_cast<const float*>(ql + 2 * QT);
+  // One query tile for this wave.  MASK tiles handle queries before a key of
+  // the block (causal) and queries or keys past the end; the others need no mask.
+  template <int BUF, bool MASK>
+  __device__ __forceinline__ void compute_tile(int qt0) {
+    const char* kl = smem + KOFF;
+    const char* sb = smem + BUF * BUFB;
+    const float* sl = reinterpret_cast<const float*>(sb);
     const float* tl = sl + BQ;
+    const char* ql = sb + STAT;
+    const char* dl = ql + QT;
     const int qw = qt0 + 32 * qh;   // first query of this wave's half
-    if (CAUSAL && qw + 31 < kw0) return;   // every query of the half precedes every key
+    if (MASK && CAUSAL && qw + 31 < kw0) return;   // every query of the half precedes every key
     // S = Q K^T and dP = dO V^T; rows: queries (sigma order), columns: keys
     f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
@@ -165,7 +182,6 @@ struct DkdvKernel {
       pacc = mfma_bf16(lds_read_b128(dl, aofs[c]), vreg[c], pacc);
     }
     // P = exp(S - LSE) and dS = P o (dP - delta), packed to BF16
-    const bool need_mask = (CAUSAL && qw < kw0 + 31) || (qw + 32 > N) || (kv0 + BKV > N);
     const float c1 = p.scale * kLog2e;
     uint32_t pP[8], pS[8];
 #pragma unroll
@@ -187,7 +203,7 @@ struct DkdvKernel {
           const float lse = (e + u) < 4 ? l0[e + u] : l1[e + u - 4];
           const float dlt = (e + u) < 4 ? d0[e + u] : d1[e + u - 4];
           float pv = fast_exp2(fmaf(sacc[r], c1, -lse * kLog2e));
-          if (need_mask) pv = ((e + u) >= vis && (e + u) < qend && mykey < N) ? pv : 0.f;
+          if (MASK) pv = ((e + u) >= vis && (e + u) < qend && mykey < N) ? pv : 0.f;
           pr[u] = pv;
           ds[u] = pv * (pacc[r] - dlt);
         }
@@ -213,10 +229,19 @@ struct DkdvKernel {
     }
   }
 
+  // Tile t of the loop (query tile qt_begin + t * BQ): start the loads of tile
+  // t + 1 into the other buffer, compute tile t, then wait for both.
+  template <int BUF, bool MASK>
+  __device__ __forceinline__ void step(int t, int n_tiles) {
+    if (t + 1 < n_tiles) issue_tile(qt_begin + (t + 1) * BQ, 1 - BUF);
+    compute_tile<BUF, MASK>(qt_begin + t * BQ);
+    wait_all_and_barrier();
+  }
+
   // Sum the partial accumulators of waves w and w + 4 (same keys, other query
   // half) through LDS and store the gradient from waves 0..3.
   __device__ __forceinline__ void reduce_store(f32x16* acc, uint16_t* out, float mul) {
-    f32x4* red = reinterpret_cast<f32x4*>(smem + KBLK);   // 4 waves x DB x 16 floats x 64 lanes
+    f32x4* red = reinterpret_cast<f32x4*>(smem);   // 4 waves x DB x 16 floats x 64 lanes
     if (qh == 1) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -245,7 +270,7 @@ struct DkdvKernel {
   __device__ __forceinline__ void run() {
     tid = threadIdx.x;
     lane = tid & 63;
-    w = tid >> 6;
+    w = __builtin_amdgcn_readfirstlane(tid >> 6);
     hi = lane >> 5;
     kb = w & 3;
     qh = w >> 2;
@@ -253,10 +278,12 @@ struct DkdvKernel {
     int kvb;
     map_kv_block(blockIdx.x, p.BH, bh, kvb);
     base = (size_t)bh * N * D;
-    Q = p.q + base;
-    DO = p.dout + base;
     const uint16_t* K = p.k + base;
     const uint16_t* V = p.v + base;
+    qrs = make_rsrc(p.q + base, N * D * 2);
+    dors = make_rsrc(p.dout + base, N * D * 2);
+    lrs = make_rsrc(p.lse + (size_t)bh * N, N * 4);
+    drs = make_rsrc(p.delta + (size_t)bh * N, N * 4);
     kv0 = kvb * BKV;
     kw0 = kv0 + 32 * kb;
     mykey = kw0 + (lane & 31);
@@ -267,7 +294,8 @@ struct DkdvKernel {
       const int slot = (w * KLOADS + i) * 64 + lane;
       const int row = slot / CH, pchunk = slot % CH;
       const int key = min(kv0 + row, N - 1);
-      g2lds_b128(K + (size_t)key * D + (pchunk ^ swz_pattern<CH>(row)) * 8, smem + (w * KLOADS + i) * 1024);
+      g2lds_b128(K + (size_t)key * D + (pchunk ^ swz_pattern<CH>(row)) * 8,
+                 smem + KOFF + (w * KLOADS + i) * 1024);
     }
 #pragma unroll
     for (int c = 0; c < DC; ++c)
@@ -276,8 +304,7 @@ struct DkdvKernel {
     for (int i = 0; i < LOADS; ++i) {
       const int slot = (w * LOADS + i) * 64 + lane;
       const int row = slot / CH, pchunk = slot % CH;
-      grow[i] = row;
-      goff[i] = row * D + (pchunk ^ swz_pattern<CH>(row)) * 8;
+      voff[i] = (row * D + (pchunk ^ swz_pattern<CH>(row)) * 8) * 2;
     }
     const int arow = 32 * qh + sigma32(lane & 31);
 #pragma unroll
@@ -298,15 +325,29 @@ struct DkdvKernel {
       dkacc[db] = f32x16{};
     }
 
-    const int qt_begin = CAUSAL ? kv0 : 0;
-    if (qt_begin < N) issue_tile(qt_begin, 0);
+    // Query tiles qt_begin + t * BQ, t < n_tiles.  Under a causal mask the first
+    // two overlap the key block and need the mask; a ragged last tile needs it
+    // for the queries past N.  The tiles in between run unmasked, in pairs so
+    // that the buffer index stays a compile-time constant.
+    qt_begin = CAUSAL ? kv0 : 0;
+    const int n_tiles = (N - qt_begin + BQ - 1) / BQ;
+    const int n_full = (N - qt_begin) / BQ;
+    const int n_lead = CAUSAL ? min(2, n_tiles) : 0;
+    if (n_tiles > 0) issue_tile(qt_begin, 0);
     wait_all_and_barrier();
-    int buf = 0;
-    for (int qt0 = qt_begin; qt0 < N; qt0 += BQ) {
-      if (qt0 + BQ < N) issue_tile(qt0 + BQ, buf ^ 1);
-      compute_tile(qt0, buf);
-      wait_all_and_barrier();
-      buf ^= 1;
+    int t = 0;
+    for (; t + 2 <= n_lead; t += 2) {
+      step<0, true>(t, n_tiles);
+      step<1, true>(t + 1, n_tiles);
+    }
+    if (t == n_lead)
+      for (; t + 2 <= n_full; t += 2) {
+        step<0, false>(t, n_tiles);
+        step<1, false>(t + 1, n_tiles);
+      }
+    for (; t < n_tiles; t += 2) {
+      step<0, true>(t, n_tiles);
+      if (t + 1 < n_tiles) step<1, true>(t + 1, n_tiles);
     }
     reduce_store(dvacc, p.dv, 1.f);
     reduce_store(dkacc, p.dk, p.scale);
@@ -317,7 +358,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(DkdvParams p) {
   using Kt = DkdvKernel<D, CAUSAL>;
   constexpr int RED = 4 * (D / 32) * 4 * 64 * 16;   // reduction area, inside the tile buffers
-  constexpr int SMEM = Kt::KBLK + 2 * Kt::BUFB;
+  constexpr int SMEM = Kt::KOFF + Kt::KBLK;
   static_assert(RED <= 2 * Kt::BUFB, "reduction area must fit the tile buffers");
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
   Kt k(p, smem);

@@ -70,8 +70,8 @@ struct DqKernel {
   size_t base;
   const uint16_t* K;
   const uint16_t* V;
-  int goff[LOADS];
-  int grow[LOADS];
+  __amdgpu_buffer_rsrc_t krs, vrs;
+  int voff[LOADS];
   int kofs[DC];
   int tofs[2][DB];
   u32x4 qreg[DC];
@@ -84,20 +84,39 @@ struct DqKernel {
   __device__ __forceinline__ void issue_tile(int j, int buf) {
     const int kv0 = j * BN;
     char* kl = smem + buf * 2 * TILE;
+    if (kv0 + BN <= N) {
+      // whole tile inside the slice: per-lane offsets fixed, tile offset scalar
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      int off = kv0 * D + goff[i];
-      if (kv0 + BN > N && kv0 + grow[i] >= N) off = (N - 1) * D + (goff[i] - grow[i] * D);
-      char* dst = kl + (w * LOADS + i) * 1024;
-      g2lds_b128(K + off, dst);
-      g2lds_b128(V + off, dst + TILE);
+      for (int i = 0; i < LOADS; ++i) {
+        char* dst = kl + (w * LOADS + i) * 1024;
+        buf2lds_b128(krs, voff[i], kv0 * D * 2, dst);
+        buf2lds_b128(vrs, voff[i], kv0 * D * 2, dst + TILE);
+      }
+    } else {
+      // ragged last tile: rows past the end repeat row N-1 (masked later)
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int slot = (w * LOADS + i) * 64 + lane;
+        const int row = slot / CH;
+        const int off = voff[i] + (min(kv0 + row, N - 1) - row) * D * 2;
+        char* dst = kl + (w * LOADS + i) * 1024;
+        buf2lds_b128(krs, off, 0, dst);
+        buf2lds_b128(vrs, off, 0, dst + TILE);
+      }
     }
   }
 
-  template <int BUF>
+  // Tile j for this wave; MASK tiles handle keys after a query of the workgroup
+  // (causal) or past the sequence end, the others are fully visible.
+  template <int BUF, bool MASK>
   __device__ __forceinline__ void compute_tile(int j) {
     const int kv0 = j * BN;
-    if (!(qw0 < N && (!CAUSAL || kv0 <= qw0 + 31))) return;
+    if (MASK && !(qw0 < N && (!CAUSAL || kv0 <= qw0 + 31))) return;  // no key of this tile is visible
+    tile<BUF, MASK>(kv0);
+  }
+
+  template <int BUF, bool MASK>
+  __device__ __forceinline__ void tile(int kv0) {
     const char* kl = smem + BUF * 2 * TILE;
     const char* vl = kl + TILE;
     f32x16 sacc[KB], pacc[KB];
@@ -111,7 +130,6 @@ struct DqKernel {
         pacc[kb] = mfma_bf16(lds_read_b128(vl, kofs[c] + kb * 32 * ROWB), doreg[c], pacc[kb]);
       }
     }
-    const bool need_mask = (CAUSAL && kv0 + BN - 1 > qw0) || (kv0 + BN > N);
     const int lim = (CAUSAL ? min(myq, N - 1) : N - 1) - (kv0 + 8 * hi);
     const float c1 = p.scale * kLog2e;
     uint32_t pk[KB][8];
@@ -124,7 +142,7 @@ struct DqKernel {
         for (int e = 0; e < 2; ++e) {
           const int r = 2 * i + e;
           float pr = fast_exp2(fmaf(sacc[kb][r], c1, -lse2));
-          if (need_mask) {
+          if (MASK) {
             const int off = 32 * kb + 16 * (r >> 3) + (r & 7);
             pr = off > lim ? 0.f : pr;
           }
@@ -146,17 +164,17 @@ struct DqKernel {
     }
   }
 
-  template <int BUF>
+  template <int BUF, bool MASK>
   __device__ __forceinline__ void step(int j, int n_tiles) {
     if (j + 1 < n_tiles) issue_tile(j + 1, 1 - BUF);
-    compute_tile<BUF>(j);
+    compute_tile<BUF, MASK>(j);
     wait_all_and_barrier();
   }
 
   __device__ __forceinline__ void run() {
     tid = threadIdx.x;
     lane = tid & 63;
-    w = tid >> 6;
+    w = __builtin_amdgcn_readfirstlane(tid >> 6);
     hi = lane >> 5;
     N = p.N;
     int qb;
@@ -165,6 +183,8 @@ struct DqKernel {
     const uint16_t* Q = p.q + base;
     K = p.k + base;
     V = p.v + base;
+    krs = make_rsrc(K, N * D * 2);
+    vrs = make_rsrc(V, N * D * 2);
     q0 = qb * BM;
     qw0 = q0 + 32 * w;
     myq = qw0 + (lane & 31);
@@ -182,8 +202,7 @@ struct DqKernel {
     for (int i = 0; i < LOADS; ++i) {
       const int slot = (w * LOADS + i) * 64 + lane;
       const int row = slot / CH, pchunk = slot % CH;
-      grow[i] = row;
-      goff[i] = row * D + (pchunk ^ swz_pattern<CH>(row)) * 8;
+      voff[i] = (row * D + (pchunk ^ swz_pattern<CH>(row)) * 8) * 2;
     }
     const int krow = sigma32(lane & 31);
 #pragma unroll
@@ -202,9 +221,18 @@ struct DqKernel {
     const int n_tiles = (kv_end + BN - 1) / BN;
     issue_tile(0, 0);
     wait_all_and_barrier();
-    for (int j = 0; j < n_tiles; j += 2) {
-      step<0>(j, n_tiles);
-      if (j + 1 < n_tiles) step<1>(j + 1, n_tiles);
+    // Leading tiles that need no mask for any wave of the workgroup (all keys
+    // before the first query, none past N) run unmasked, in pairs so that the
+    // buffer index stays a compile-time constant; the rest run masked.
+    const int n_plain = CAUSAL ? min(q0, N) / BN : N / BN;
+    int j = 0;
+    for (; j + 2 <= n_plain; j += 2) {
+      step<0, false>(j, n_tiles);
+      step<1, false>(j + 1, n_tiles);
+    }
+    for (; j < n_tiles; j += 2) {
+      step<0, true>(j, n_tiles);
+      if (j + 1 < n_tiles) step<1, true>(j + 1, n_tiles);
     }
     // dQ = scale * dQ^T; lane holds query myq, features 32db + 8(r/4) + 4hi + r%4
     if (!valid) return;

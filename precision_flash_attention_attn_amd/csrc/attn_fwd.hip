@@ -43,6 +43,11 @@ struct FwdParams {
   int32_t* flags;
   int BH, N, n_qblocks;
   float scale, beta, eps;
+  // +inf and -inf, passed in so that max(a, b) = med3(a, b, +inf) and
+  // min(a, b) = med3(a, b, -inf) stay single v_med3_f32 instructions (a
+  // literal infinity is folded back into fmaxf/fminf, which the compiler
+  // surrounds with NaN-quieting copies of both operands)
+  float pinf, ninf;
 };
 
 // Row order of K inside a 32-key block: MFMA accumulator row i of lane half h
@@ -87,8 +92,8 @@ struct FwdKernel {
   size_t base;
   const uint16_t* K;
   const uint16_t* V;
-  int goff[LOADS];       // element offset (row * D + chunk * 8) of this lane's direct loads
-  int grow[LOADS];       // tile row of each direct load
+  __amdgpu_buffer_rsrc_t krs, vrs;  // this slice of K and V
+  int voff[LOADS];       // byte offset in the tile (row * D + swizzled chunk * 8) * 2 of this lane's direct loads
   int kofs[DC];          // LDS byte offsets of the K operand reads (block 0, buffer 0)
   int vofs[2][DB];       // LDS byte offsets of the V transpose reads (chunk 0, buffer 0)
   u32x4 qreg[DC];
@@ -102,20 +107,39 @@ struct FwdKernel {
   __device__ __forceinline__ void issue_tile(int j, int buf) {
     const int kv0 = j * BN;
     char* kl = smem + buf * 2 * TILE;
+    if (kv0 + BN <= N) {
+      // whole tile inside the slice: per-lane offsets fixed, tile offset scalar
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      int off = kv0 * D + goff[i];
-      if (kv0 + BN > N && kv0 + grow[i] >= N) off = (N - 1) * D + (goff[i] - grow[i] * D);
-      char* dst = kl + (w * LOADS + i) * 1024;
-      g2lds_b128(K + off, dst);
-      g2lds_b128(V + off, dst + TILE);
+      for (int i = 0; i < LOADS; ++i) {
+        char* dst = kl + (w * LOADS + i) * 1024;
+        buf2lds_b128(krs, voff[i], kv0 * D * 2, dst);
+        buf2lds_b128(vrs, voff[i], kv0 * D * 2, dst + TILE);
+      }
+    } else {
+      // ragged last tile: rows past the end repeat row N-1 (masked later)
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int slot = (w * LOADS + i) * 64 + lane;
+        const int row = slot / CH;
+        const int off = voff[i] + (min(kv0 + row, N - 1) - row) * D * 2;
+        char* dst = kl + (w * LOADS + i) * 1024;
+        buf2lds_b128(krs, off, 0, dst);
+        buf2lds_b128(vrs, off, 0, dst + TILE);
+      }
     }
   }
 
-  template <int BUF>
+  // Tile j for this wave; MASK tiles handle keys after a query of the workgroup
+  // (causal) or past the sequence end, the others are fully visible.
+  template <int BUF, bool MASK>
   __device__ __forceinline__ void compute_tile(int j) {
     const int kv0 = j * BN;
-    if (!(qw0 < N && (!CAUSAL || kv0 <= qw0 + 31))) return;  // no key of this tile is visible
+    if (MASK && !(qw0 < N && (!CAUSAL || kv0 <= qw0 + 31))) return;  // no key of this tile is visible
+    tile<BUF, MASK>(kv0);
+  }
+
+  template <int BUF, bool MASK>
+  __device__ __forceinline__ void tile(int kv0) {
     const char* kl = smem + BUF * 2 * TILE;
     const char* vl = kl + TILE;
     f32x16 sacc[KB];
@@ -127,8 +151,7 @@ struct FwdKernel {
         sacc[kb] = mfma_bf16(lds_read_b128(kl, kofs[c] + kb * 32 * ROWB), qreg[c], sacc[kb]);
     }
     // mask keys after the query (causal) and beyond the sequence, branch-free
-    const bool need_mask = (CAUSAL && kv0 + BN - 1 > qw0) || (kv0 + BN > N);
-    if (need_mask) {
+    if (MASK) {
       const int lim = (CAUSAL ? min(myq, N - 1) : N - 1) - (kv0 + 8 * hi);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -139,24 +162,26 @@ struct FwdKernel {
         }
     }
     // tile maximum (and second largest, as a multiset) of the raw dot products
+    const float hv = p.pinf, lv = p.ninf;
     float t1 = kNegInf, t2 = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         if (FLAGS) t2 = med3(t1, t2, sacc[kb][r]);
-        t1 = fmaxf(t1, sacc[kb][r]);
+        t1 = med3(t1, sacc[kb][r], hv);
       }
     // combine the two lane halves that share a query
     float a1, b1;
     pair32(t1, a1, b1);
+    const float tmax = med3(a1, b1, hv);
     if (FLAGS) {
       float a2, b2;
       pair32(t2, a2, b2);
-      t2 = fmaxf(fminf(a1, b1), fmaxf(a2, b2));
-      M2raw = fmaxf(fminf(Mraw, fmaxf(a1, b1)), fmaxf(M2raw, t2));
+      t2 = med3(med3(a1, b1, lv), med3(a2, b2, hv), hv);
+      M2raw = med3(med3(Mraw, tmax, lv), med3(M2raw, t2, hv), hv);
     }
-    Mraw = fmaxf(Mraw, fmaxf(a1, b1));
+    Mraw = med3(Mraw, tmax, hv);
     // S-unit maximum, tie flag and shift (section 3.4.5)
     const float Ms = Mraw * p.scale;
     if (FLAGS) flag = (M2raw != kNegInf) && (Ms - M2raw * p.scale <= p.eps);
@@ -214,17 +239,17 @@ struct FwdKernel {
     }
   }
 
-  template <int BUF>
+  template <int BUF, bool MASK>
   __device__ __forceinline__ void step(int j, int n_tiles) {
     if (j + 1 < n_tiles) issue_tile(j + 1, 1 - BUF);
-    compute_tile<BUF>(j);
+    compute_tile<BUF, MASK>(j);
     wait_all_and_barrier();
   }
 
   __device__ __forceinline__ void run() {
     tid = threadIdx.x;
     lane = tid & 63;
-    w = tid >> 6;
+    w = __builtin_amdgcn_readfirstlane(tid >> 6);
     hi = lane >> 5;
     N = p.N;
     int qb;
@@ -233,6 +258,8 @@ struct FwdKernel {
     const uint16_t* Q = p.q + base;
     K = p.k + base;
     V = p.v + base;
+    krs = make_rsrc(K, N * D * 2);
+    vrs = make_rsrc(V, N * D * 2);
     q0 = qb * BM;
     qw0 = q0 + 32 * w;
     myq = qw0 + (lane & 31);
@@ -245,8 +272,7 @@ struct FwdKernel {
     for (int i = 0; i < LOADS; ++i) {
       const int slot = (w * LOADS + i) * 64 + lane;
       const int row = slot / CH, pchunk = slot % CH;
-      grow[i] = row;
-      goff[i] = row * D + (pchunk ^ swz_pattern<CH>(row)) * 8;
+      voff[i] = (row * D + (pchunk ^ swz_pattern<CH>(row)) * 8) * 2;
     }
     const int krow = sigma32(lane & 31);
 #pragma unroll
@@ -270,9 +296,18 @@ struct FwdKernel {
     const int n_tiles = (kv_end + BN - 1) / BN;
     issue_tile(0, 0);
     wait_all_and_barrier();
-    for (int j = 0; j < n_tiles; j += 2) {
-      step<0>(j, n_tiles);
-      if (j + 1 < n_tiles) step<1>(j + 1, n_tiles);
+    // Leading tiles that need no mask for any wave of the workgroup (all keys
+    // before the first query, none past N) run unmasked, in pairs so that the
+    // buffer index stays a compile-time constant; the rest run masked.
+    const int n_plain = CAUSAL ? min(q0, N) / BN : N / BN;
+    int j = 0;
+    for (; j + 2 <= n_plain; j += 2) {
+      step<0, false>(j, n_tiles);
+      step<1, false>(j + 1, n_tiles);
+    }
+    for (; j < n_tiles; j += 2) {
+      step<0, true>(j, n_tiles);
+      if (j + 1 < n_tiles) step<1, true>(j + 1, n_tiles);
     }
     epilogue();
   }
@@ -331,6 +366,8 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   p.scale = a.scale;
   p.beta = a.beta;
   p.eps = a.eps;
+  p.pinf = __builtin_inff();
+  p.ninf = -__builtin_inff();
   const unsigned grid = (unsigned)(p.BH * p.n_qblocks);
   hipLaunchKernelGGL((fwd_kernel<D, MODE, CAUSAL, FLAGS>), dim3(grid), dim3(256), 0, stream, p);
   return hipGetLastError();

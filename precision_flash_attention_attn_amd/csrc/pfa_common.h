@@ -58,6 +58,7 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ float med3(float a, float b, float c) { return __builtin_amdgcn_fmed3f(a, b, c); }
 
+
 // Exchange with the lane 32 positions away (the other half of the wave).
 __device__ __forceinline__ float xchg32(float x) { return __shfl_xor(x, 32, 64); }
 
@@ -123,6 +124,21 @@ __device__ __forceinline__ u32x4 ldg_b128(const void* p) { return *reinterpret_c
 // same for the whole wave.  Completion is tracked by vmcnt.
 __device__ __forceinline__ void g2lds_b128(const void* gptr, char* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+
+// Buffer resource for raw byte-offset loads from base .. base + bytes - 1
+// (stride 0, 32-bit data format word of the gfx9 family).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// Direct buffer -> LDS load of 16 bytes per lane (buffer_load_dwordx4 ... lds)
+// from byte offset voff + soff of the resource: lane l's bytes land at
+// lds_wave_base + 16 * l.  soff and lds_wave_base must be wave-uniform.
+__device__ __forceinline__ void buf2lds_b128(__amdgpu_buffer_rsrc_t r, int voff, int soff,
+                                             char* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base,
+                                           16, voff, soff, 0, 0);
 }
 
 // Wait for every outstanding memory operation of this wave (including direct

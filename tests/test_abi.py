@@ -84,6 +84,9 @@ def test_fwd_rejects_invalid_arguments(L):
     assert _fwd(L, opts=bnd.TieOpts(2.0, -1e-3)) == inv
     assert _fwd(L, opts=bnd.TieOpts(2.0, float("nan"))) == inv
     assert _fwd(L, B=1 << 16, H=1 << 16, N=1 << 10, d=128) == inv   # too many elements
+    # one (batch, head) slice must keep 32-bit byte offsets: N*d < 2^29
+    assert _fwd(L, N=1 << 22, d=128) == uns
+    assert _fwd(L, N=(1 << 22) - 1, d=128, q=None) == inv   # size accepted, then the NULL q
 
 
 def _bwd(L, ws=FAKE, ws_bytes=1 << 30, q=FAKE, dq=FAKE, o=FAKE, B=1, H=1, N=128, d=64, mode=0,
@@ -105,6 +108,7 @@ def test_bwd_rejects_invalid_arguments(L):
     assert _bwd(L, mode=5) == inv
     assert _bwd(L, scale=float("inf")) == inv
     assert _bwd(L, delta=FAKE + 1) == inv
+    assert _bwd(L, N=1 << 23, d=64) == uns
 
 
 def test_python_binding_validates_before_calling(L):
