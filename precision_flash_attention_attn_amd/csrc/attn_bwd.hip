@@ -113,27 +113,35 @@ struct DkdvKernel {
   static constexpr int KBLK = BKV * D * 2;           // bytes of the key block
   static constexpr int STAT = 2 * BQ * 4;            // LSE and delta of a query tile
   static constexpr int BUFB = STAT + 2 * QT;         // one tile buffer: LSE, delta, Q, dO
-  static constexpr int KOFF = 2 * BUFB;              // the key block follows the two buffers
   static constexpr int LOADS = QT / (NT * 16);       // direct loads per thread per tile
   static constexpr int KLOADS = KBLK / (NT * 16);    // direct loads per thread for the key block
 
   const DkdvParams& p;
-  char* smem;   // [buffer 0 | buffer 1 | key block]
+  // Separate LDS arrays for the key block and the two stage buffers: the
+  // compiler can then tell that the direct loads into one buffer never alias
+  // reads of the other and does not wait for the loads in flight.
+  char* kls;
+  char* sm0;
+  char* sm1;
   int tid, lane, w, hi, kb, qh, N, bh, kv0, kw0, mykey, qt_begin;
   size_t base;
   __amdgpu_buffer_rsrc_t qrs, dors, lrs, drs;   // this slice of Q, dO, LSE, delta
   int voff[LOADS];   // byte offset in a tile of this lane's direct loads
-  int aofs[DC];      // LDS offsets of the Q / dO operand reads (this wave's query half)
-  int kofs[DC];      // LDS offsets of the K operand reads (this wave's keys)
-  int tofs[2][DB];   // LDS offsets of the transpose reads
+  // LDS offsets of the operand reads at contraction step 0 (feature block 0):
+  // Q / dO rows of this wave's query half, K rows of its keys, and the two
+  // transpose reads.  Step c (block db) is the offset XOR 32c (XOR 64db), as
+  // the swizzle only permutes chunks inside a row.
+  int abase, kbase, tbase[2];
   u32x4 vreg[DC];
   f32x16 dvacc[DB], dkacc[DB];
 
-  __device__ DkdvKernel(const DkdvParams& p_, char* smem_) : p(p_), smem(smem_) {}
+  __device__ DkdvKernel(const DkdvParams& p_, char* kl_, char* s0, char* s1)
+      : p(p_), kls(kl_), sm0(s0), sm1(s1) {}
 
-  // Direct loads of the query tile at qt0 (Q, dO, LSE, delta) into buffer buf.
-  __device__ __forceinline__ void issue_tile(int qt0, int buf) {
-    char* bl = smem + buf * BUFB;
+  // Direct loads of the query tile at qt0 (Q, dO, LSE, delta) into buffer BUF.
+  template <int BUF>
+  __device__ __forceinline__ void issue_tile(int qt0) {
+    char* bl = BUF ? sm1 : sm0;
     if (qt0 + BQ <= N) {
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
@@ -166,20 +174,25 @@ struct DkdvKernel {
   // the block (causal) and queries or keys past the end; the others need no mask.
   template <int BUF, bool MASK>
   __device__ __forceinline__ void compute_tile(int qt0) {
-    const char* kl = smem + KOFF;
-    const char* sb = smem + BUF * BUFB;
+    const char* kl = kls;
+    const char* sb = BUF ? sm1 : sm0;
     const float* sl = reinterpret_cast<const float*>(sb);
     const float* tl = sl + BQ;
     const char* ql = sb + STAT;
     const char* dl = ql + QT;
     const int qw = qt0 + 32 * qh;   // first query of this wave's half
     if (MASK && CAUSAL && qw + 31 < kw0) return;   // every query of the half precedes every key
+    // The per-step offsets are rebuilt from the bases in every tile (one XOR
+    // each): kept live across the loop they would push the kernel past 256
+    // VGPRs.  The empty asm hides the bases' values so the XORs stay here.
+    int ab = abase, kbs = kbase, t0 = tbase[0], t1 = tbase[1];
+    asm volatile("" : "+v"(ab), "+v"(kbs), "+v"(t0), "+v"(t1));
     // S = Q K^T and dP = dO V^T; rows: queries (sigma order), columns: keys
     f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
-      sacc = mfma_bf16(lds_read_b128(ql, aofs[c]), lds_read_b128(kl, kofs[c]), sacc);
-      pacc = mfma_bf16(lds_read_b128(dl, aofs[c]), vreg[c], pacc);
+      sacc = mfma_bf16(lds_read_b128(ql, ab ^ (32 * c)), lds_read_b128(kl, kbs ^ (32 * c)), sacc);
+      pacc = mfma_bf16(lds_read_b128(dl, ab ^ (32 * c)), vreg[c], pacc);
     }
     // P = exp(S - LSE) and dS = P o (dP - delta), packed to BF16
     const float c1 = p.scale * kLog2e;
@@ -219,11 +232,11 @@ struct DkdvKernel {
       const u32x4 bS = u32x4{pS[o4], pS[o4 + 1], pS[o4 + 2], pS[o4 + 3]};
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const u32x2 a0 = lds_read_tr(dl, tofs[0][db] + h2 * 16 * ROWB);
-        const u32x2 a1 = lds_read_tr(dl, tofs[1][db] + h2 * 16 * ROWB);
+        const u32x2 a0 = lds_read_tr(dl, (t0 ^ (64 * db)) + h2 * 16 * ROWB);
+        const u32x2 a1 = lds_read_tr(dl, (t1 ^ (64 * db)) + h2 * 16 * ROWB);
         dvacc[db] = mfma_bf16(u32x4{a0.x, a0.y, a1.x, a1.y}, bP, dvacc[db]);
-        const u32x2 b0 = lds_read_tr(ql, tofs[0][db] + h2 * 16 * ROWB);
-        const u32x2 b1 = lds_read_tr(ql, tofs[1][db] + h2 * 16 * ROWB);
+        const u32x2 b0 = lds_read_tr(ql, (t0 ^ (64 * db)) + h2 * 16 * ROWB);
+        const u32x2 b1 = lds_read_tr(ql, (t1 ^ (64 * db)) + h2 * 16 * ROWB);
         dkacc[db] = mfma_bf16(u32x4{b0.x, b0.y, b1.x, b1.y}, bS, dkacc[db]);
       }
     }
@@ -233,21 +246,24 @@ struct DkdvKernel {
   // t + 1 into the other buffer, compute tile t, then wait for both.
   template <int BUF, bool MASK>
   __device__ __forceinline__ void step(int t, int n_tiles) {
-    if (t + 1 < n_tiles) issue_tile(qt_begin + (t + 1) * BQ, 1 - BUF);
+    if (t + 1 < n_tiles) issue_tile<1 - BUF>(qt_begin + (t + 1) * BQ);
     compute_tile<BUF, MASK>(qt_begin + t * BQ);
     wait_all_and_barrier();
   }
 
   // Sum the partial accumulators of waves w and w + 4 (same keys, other query
-  // half) through LDS and store the gradient from waves 0..3.
+  // half) through LDS and store the gradient from waves 0..3.  The exchange
+  // area (DB x 16 floats x 64 lanes per key group) of key groups 0, 1 is in
+  // buffer 0, of groups 2, 3 in buffer 1.
   __device__ __forceinline__ void reduce_store(f32x16* acc, uint16_t* out, float mul) {
-    f32x4* red = reinterpret_cast<f32x4*>(smem);   // 4 waves x DB x 16 floats x 64 lanes
+    f32x4* red = reinterpret_cast<f32x4*>(kb < 2 ? sm0 : sm1);
+    const int kg = kb & 1;
     if (qh == 1) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          red[((kb * DB + db) * 4 + j) * 64 + lane] =
+          red[((kg * DB + db) * 4 + j) * 64 + lane] =
               f32x4{acc[db][4 * j], acc[db][4 * j + 1], acc[db][4 * j + 2], acc[db][4 * j + 3]};
     }
     __syncthreads();
@@ -257,7 +273,7 @@ struct DkdvKernel {
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const f32x4 o = red[((kb * DB + db) * 4 + j) * 64 + lane];
+          const f32x4 o = red[((kg * DB + db) * 4 + j) * 64 + lane];
           const int d0 = 32 * db + 8 * j + 4 * hi;
           const u32x2 v = {pack_bf16(mul * (acc[db][4 * j] + o[0]), mul * (acc[db][4 * j + 1] + o[1])),
                            pack_bf16(mul * (acc[db][4 * j + 2] + o[2]), mul * (acc[db][4 * j + 3] + o[3]))};
@@ -295,7 +311,7 @@ struct DkdvKernel {
       const int row = slot / CH, pchunk = slot % CH;
       const int key = min(kv0 + row, N - 1);
       g2lds_b128(K + (size_t)key * D + (pchunk ^ swz_pattern<CH>(row)) * 8,
-                 smem + KOFF + (w * KLOADS + i) * 1024);
+                 kls + (w * KLOADS + i) * 1024);
     }
 #pragma unroll
     for (int c = 0; c < DC; ++c)
@@ -307,18 +323,13 @@ struct DkdvKernel {
       voff[i] = (row * D + (pchunk ^ swz_pattern<CH>(row)) * 8) * 2;
     }
     const int arow = 32 * qh + sigma32(lane & 31);
-#pragma unroll
-    for (int c = 0; c < DC; ++c) {
-      aofs[c] = swz<CH>(arow, 2 * c + hi);
-      kofs[c] = swz<CH>(32 * kb + (lane & 31), 2 * c + hi);
-    }
+    abase = swz<CH>(arow, hi);
+    kbase = swz<CH>(32 * kb + (lane & 31), hi);
     const int g = lane >> 4, s = lane & 15;
     const int tr_row = 32 * qh + 8 * (g >> 1) + (s >> 2);
     const int tr_col = 16 * (g & 1) + 4 * (s & 3);
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) tofs[hh][db] = swz_elem<CH>(tr_row + 4 * hh, 32 * db + tr_col);
+    tbase[0] = swz_elem<CH>(tr_row, tr_col);
+    tbase[1] = swz_elem<CH>(tr_row + 4, tr_col);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       dvacc[db] = f32x16{};
@@ -333,7 +344,7 @@ struct DkdvKernel {
     const int n_tiles = (N - qt_begin + BQ - 1) / BQ;
     const int n_full = (N - qt_begin) / BQ;
     const int n_lead = CAUSAL ? min(2, n_tiles) : 0;
-    if (n_tiles > 0) issue_tile(qt_begin, 0);
+    if (n_tiles > 0) issue_tile<0>(qt_begin);
     wait_all_and_barrier();
     int t = 0;
     for (; t + 2 <= n_lead; t += 2) {
@@ -357,11 +368,12 @@ struct DkdvKernel {
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(DkdvParams p) {
   using Kt = DkdvKernel<D, CAUSAL>;
-  constexpr int RED = 4 * (D / 32) * 4 * 64 * 16;   // reduction area, inside the tile buffers
-  constexpr int SMEM = Kt::KOFF + Kt::KBLK;
-  static_assert(RED <= 2 * Kt::BUFB, "reduction area must fit the tile buffers");
-  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
-  Kt k(p, smem);
+  constexpr int RED = 2 * (D / 32) * 4 * 64 * 16;   // exchange area of two key groups
+  static_assert(RED <= Kt::BUFB, "the exchange area must fit one tile buffer");
+  __shared__ __attribute__((aligned(1024))) char kl[Kt::KBLK];
+  __shared__ __attribute__((aligned(1024))) char s0[Kt::BUFB];
+  __shared__ __attribute__((aligned(1024))) char s1[Kt::BUFB];
+  Kt k(p, kl, s0, s1);
   k.run();
 }
 

@@ -65,7 +65,11 @@ struct DqKernel {
   static constexpr int ROWB = CH * 16;
 
   const DqParams& p;
-  char* smem;
+  // The two stage buffers are separate LDS arrays: the compiler can then tell
+  // that the direct loads into one never alias reads of the other, and does
+  // not wait for the loads in flight before reading the current buffer.
+  char* sm0;
+  char* sm1;
   int tid, lane, w, hi, N, bh, qw0, myq, q0;
   size_t base;
   const uint16_t* K;
@@ -79,11 +83,12 @@ struct DqKernel {
   f32x16 dqacc[DB];
   float lse2, dlt;
 
-  __device__ DqKernel(const DqParams& p_, char* smem_) : p(p_), smem(smem_) {}
+  __device__ DqKernel(const DqParams& p_, char* s0, char* s1) : p(p_), sm0(s0), sm1(s1) {}
 
-  __device__ __forceinline__ void issue_tile(int j, int buf) {
+  template <int BUF>
+  __device__ __forceinline__ void issue_tile(int j) {
     const int kv0 = j * BN;
-    char* kl = smem + buf * 2 * TILE;
+    char* kl = BUF ? sm1 : sm0;
     if (kv0 + BN <= N) {
       // whole tile inside the slice: per-lane offsets fixed, tile offset scalar
 #pragma unroll
@@ -117,7 +122,7 @@ struct DqKernel {
 
   template <int BUF, bool MASK>
   __device__ __forceinline__ void tile(int kv0) {
-    const char* kl = smem + BUF * 2 * TILE;
+    const char* kl = BUF ? sm1 : sm0;
     const char* vl = kl + TILE;
     f32x16 sacc[KB], pacc[KB];
 #pragma unroll
@@ -166,7 +171,7 @@ struct DqKernel {
 
   template <int BUF, bool MASK>
   __device__ __forceinline__ void step(int j, int n_tiles) {
-    if (j + 1 < n_tiles) issue_tile(j + 1, 1 - BUF);
+    if (j + 1 < n_tiles) issue_tile<1 - BUF>(j + 1);
     compute_tile<BUF, MASK>(j);
     wait_all_and_barrier();
   }
@@ -219,7 +224,7 @@ struct DqKernel {
 
     const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
     const int n_tiles = (kv_end + BN - 1) / BN;
-    issue_tile(0, 0);
+    issue_tile<0>(0);
     wait_all_and_barrier();
     // Leading tiles that need no mask for any wave of the workgroup (all keys
     // before the first query, none past N) run unmasked, in pairs so that the
@@ -252,8 +257,9 @@ struct DqKernel {
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(DqParams p) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * DqKernel<D, CAUSAL>::TILE];
-  DqKernel<D, CAUSAL> k(p, smem);
+  __shared__ __attribute__((aligned(1024))) char s0[2 * DqKernel<D, CAUSAL>::TILE];
+  __shared__ __attribute__((aligned(1024))) char s1[2 * DqKernel<D, CAUSAL>::TILE];
+  DqKernel<D, CAUSAL> k(p, s0, s1);
   k.run();
 }
 

@@ -87,89 +87,89 @@ struct FwdKernel {
   static constexpr int ROWB = CH * 16;               // bytes per LDS row
 
   const FwdParams& p;
-  char* smem;
+  // K and V tiles are staged in two buffers each, four separate LDS arrays:
+  // the compiler can then tell that the direct loads into one never alias
+  // reads of another, and does not wait for loads in flight before a read.
+  char* kb0;
+  char* kb1;
+  char* vb0;
+  char* vb1;
   int tid, lane, w, hi, N, bh, qw0, myq, q0;
   size_t base;
-  const uint16_t* K;
-  const uint16_t* V;
   __amdgpu_buffer_rsrc_t krs, vrs;  // this slice of K and V
-  int voff[LOADS];       // byte offset in the tile (row * D + swizzled chunk * 8) * 2 of this lane's direct loads
-  int kofs[DC];          // LDS byte offsets of the K operand reads (block 0, buffer 0)
-  int vofs[2][DB];       // LDS byte offsets of the V transpose reads (chunk 0, buffer 0)
+  int voff[LOADS];       // byte offset in a tile, (row * D + swizzled chunk * 8) * 2, of this lane's direct loads
+  // LDS byte offsets of the K operand read (32-key block 0, contraction step
+  // 0) and of the two V transpose reads (16-key step 0, feature block 0);
+  // step c (block db) is the offset XOR 32c (XOR 64db), as the swizzle only
+  // permutes the chunks inside a row.
+  int kbase, vbase0, vbase1;
   u32x4 qreg[DC];
   f32x16 oacc[DB];
-  float Mraw, M2raw, m, lsum;
+  f32x16 scur[KB];       // raw dot products of the tile whose P-bar is next
+  float Mraw, M2raw, m, mb, alpha, lsum;
   bool flag;
 
-  __device__ FwdKernel(const FwdParams& p_, char* smem_) : p(p_), smem(smem_) {}
+  __device__ FwdKernel(const FwdParams& p_, char* k0, char* k1, char* v0, char* v1)
+      : p(p_), kb0(k0), kb1(k1), vb0(v0), vb1(v1) {}
 
-  // Direct loads of key tile j (rows kv0 .. kv0 + 63) into buffer buf.
-  __device__ __forceinline__ void issue_tile(int j, int buf) {
+  // Direct loads of rows j*BN .. j*BN + 63 of X (K or V) into dst; rows past
+  // the end of a ragged last tile repeat row N-1 (their scores are masked).
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, int j, char* dst0) {
     const int kv0 = j * BN;
-    char* kl = smem + buf * 2 * TILE;
     if (kv0 + BN <= N) {
-      // whole tile inside the slice: per-lane offsets fixed, tile offset scalar
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        char* dst = kl + (w * LOADS + i) * 1024;
-        buf2lds_b128(krs, voff[i], kv0 * D * 2, dst);
-        buf2lds_b128(vrs, voff[i], kv0 * D * 2, dst + TILE);
-      }
+      for (int i = 0; i < LOADS; ++i) buf2lds_b128(rs, voff[i], kv0 * D * 2, dst0 + (w * LOADS + i) * 1024);
     } else {
-      // ragged last tile: rows past the end repeat row N-1 (masked later)
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
-        const int slot = (w * LOADS + i) * 64 + lane;
-        const int row = slot / CH;
+        const int row = ((w * LOADS + i) * 64 + lane) / CH;
         const int off = voff[i] + (min(kv0 + row, N - 1) - row) * D * 2;
-        char* dst = kl + (w * LOADS + i) * 1024;
-        buf2lds_b128(krs, off, 0, dst);
-        buf2lds_b128(vrs, off, 0, dst + TILE);
+        buf2lds_b128(rs, off, 0, dst0 + (w * LOADS + i) * 1024);
       }
     }
   }
+  template <int B> __device__ __forceinline__ void issue_k(int j) { issue(krs, j, B ? kb1 : kb0); }
+  template <int B> __device__ __forceinline__ void issue_v(int j) { issue(vrs, j, B ? vb1 : vb0); }
 
-  // Tile j for this wave; MASK tiles handle keys after a query of the workgroup
-  // (causal) or past the sequence end, the others are fully visible.
-  template <int BUF, bool MASK>
-  __device__ __forceinline__ void compute_tile(int j) {
-    const int kv0 = j * BN;
-    if (MASK && !(qw0 < N && (!CAUSAL || kv0 <= qw0 + 31))) return;  // no key of this tile is visible
-    tile<BUF, MASK>(kv0);
-  }
-
-  template <int BUF, bool MASK>
-  __device__ __forceinline__ void tile(int kv0) {
-    const char* kl = smem + BUF * 2 * TILE;
-    const char* vl = kl + TILE;
-    f32x16 sacc[KB];
+  // S^T (64 keys x 32 queries) = K_tile Q^T from K buffer B.
+  template <int B>
+  __device__ __forceinline__ void qk(f32x16 (&s)[KB]) {
+    const char* kl = B ? kb1 : kb0;
+    int kbs = kbase;
+    asm volatile("" : "+v"(kbs));   // keep the per-step XORs here, not in live registers
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      sacc[kb] = f32x16{};
+      s[kb] = f32x16{};
 #pragma unroll
       for (int c = 0; c < DC; ++c)
-        sacc[kb] = mfma_bf16(lds_read_b128(kl, kofs[c] + kb * 32 * ROWB), qreg[c], sacc[kb]);
+        s[kb] = mfma_bf16(lds_read_b128(kl, (kbs ^ (32 * c)) + kb * 32 * ROWB), qreg[c], s[kb]);
     }
-    // mask keys after the query (causal) and beyond the sequence, branch-free
-    if (MASK) {
-      const int lim = (CAUSAL ? min(myq, N - 1) : N - 1) - (kv0 + 8 * hi);
+  }
+
+  // Keys after the query (causal) or past the sequence end get -inf.
+  __device__ __forceinline__ void mask(f32x16 (&s)[KB], int kv0) {
+    const int lim = (CAUSAL ? min(myq, N - 1) : N - 1) - (kv0 + 8 * hi);
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int off = 32 * kb + 16 * (r >> 3) + (r & 7);
-          sacc[kb][r] = off > lim ? kNegInf : sacc[kb][r];
-        }
-    }
-    // tile maximum (and second largest, as a multiset) of the raw dot products
+      for (int r = 0; r < 16; ++r) {
+        const int off = 32 * kb + 16 * (r >> 3) + (r & 7);
+        s[kb][r] = off > lim ? kNegInf : s[kb][r];
+      }
+  }
+
+  // Running maximum (and second largest, as a multiset) of the raw dot
+  // products, then the S-unit maximum, tie flag and shift (section 3.4.5):
+  // sets m, mb = m log2 e and alpha = exp(m_old - m) for the tile s.
+  __device__ __forceinline__ void update_max(const f32x16 (&s)[KB]) {
     const float hv = p.pinf, lv = p.ninf;
     float t1 = kNegInf, t2 = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        if (FLAGS) t2 = med3(t1, t2, sacc[kb][r]);
-        t1 = med3(t1, sacc[kb][r], hv);
+        if (FLAGS) t2 = med3(t1, t2, s[kb][r]);
+        t1 = med3(t1, s[kb][r], hv);
       }
     // combine the two lane halves that share a query
     float a1, b1;
@@ -182,28 +182,39 @@ struct FwdKernel {
       M2raw = med3(med3(Mraw, tmax, lv), med3(M2raw, t2, hv), hv);
     }
     Mraw = med3(Mraw, tmax, hv);
-    // S-unit maximum, tie flag and shift (section 3.4.5)
     const float Ms = Mraw * p.scale;
     if (FLAGS) flag = (M2raw != kNegInf) && (Ms - M2raw * p.scale <= p.eps);
     float m_new = Ms;
     if (TIE && flag) m_new = (Ms > 0.f) ? p.beta * Ms : ((Ms < 0.f) ? 0.f : Ms);
-    float alpha = 1.f, mb = 0.f;
+    alpha = 1.f;
     if (m_new != kNegInf) {
       alpha = (m == kNegInf) ? 0.f : fast_exp2((m - m_new) * kLog2e);
       mb = m_new * kLog2e;
       m = m_new;
     }
+  }
+
+  // O-bar *= alpha, skipped when no query of the wave changed its maximum.
+  __device__ __forceinline__ void rescale() {
+    if (!__all(alpha == 1.f)) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+  }
+
+  // P-bar = exp(S - m) rounded to BF16 (plus the BF16 remainder in the FP32
+  // output mode), and l = l alpha + its row sum.
+  __device__ __forceinline__ void softmax(const f32x16 (&s)[KB], uint32_t (&pk)[KB][8], uint32_t (&pl)[KB][8]) {
     const float c1 = p.scale * kLog2e;
-    // P-bar = exp(S - m), rounded to BF16 (or split hi + lo), and its row sum
-    uint32_t pk[KB][8];
-    uint32_t pl[KB][8];
     float lt = 0.f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float pa = fast_exp2(fmaf(sacc[kb][2 * i], c1, -mb));
-        const float pb = fast_exp2(fmaf(sacc[kb][2 * i + 1], c1, -mb));
+        const float pa = fast_exp2(fmaf(s[kb][2 * i], c1, -mb));
+        const float pb = fast_exp2(fmaf(s[kb][2 * i + 1], c1, -mb));
         const uint32_t u = pack_bf16(pa, pb);
         pk[kb][i] = u;
         lt = add_bf16_pair(u, lt);
@@ -214,21 +225,22 @@ struct FwdKernel {
         }
       }
     lsum = fmaf(lsum, alpha, lt);
-    if (!__all(alpha == 1.f)) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-    }
-    // O^T += V^T P-bar^T
+  }
+
+  // O^T += V^T P-bar^T from V buffer B.
+  template <int B>
+  __device__ __forceinline__ void pv(const uint32_t (&pk)[KB][8], const uint32_t (&pl)[KB][8]) {
+    const char* vl = B ? vb1 : vb0;
+    int v0s = vbase0, v1s = vbase1;
+    asm volatile("" : "+v"(v0s), "+v"(v1s));
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
       const int kb = kc >> 1, o4 = 4 * (kc & 1);
       const u32x4 bop = u32x4{pk[kb][o4], pk[kb][o4 + 1], pk[kb][o4 + 2], pk[kb][o4 + 3]};
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const u32x2 a0 = lds_read_tr(vl, vofs[0][db] + kc * 16 * ROWB);
-        const u32x2 a1v = lds_read_tr(vl, vofs[1][db] + kc * 16 * ROWB);
+        const u32x2 a0 = lds_read_tr(vl, (v0s ^ (64 * db)) + kc * 16 * ROWB);
+        const u32x2 a1v = lds_read_tr(vl, (v1s ^ (64 * db)) + kc * 16 * ROWB);
         const u32x4 aop = u32x4{a0.x, a0.y, a1v.x, a1v.y};
         oacc[db] = mfma_bf16(aop, bop, oacc[db]);
         if (HP) {
@@ -239,11 +251,35 @@ struct FwdKernel {
     }
   }
 
-  template <int BUF, bool MASK>
+  // Loop step j (P = j mod 2): tile j is finished (P-bar, O-bar update) while
+  // the scores of tile j + 1 are computed and reduced, so the MFMA and VALU
+  // work of consecutive tiles can interleave.  K runs one tile ahead of V:
+  // K(j+1) sits in K buffer 1-P, V(j) in V buffer P; the loads of V(j+1) and
+  // K(j+2) go into the buffers that step j-1 finished with.
+  template <int P, bool MASKN>
   __device__ __forceinline__ void step(int j, int n_tiles) {
-    if (j + 1 < n_tiles) issue_tile(j + 1, 1 - BUF);
-    compute_tile<BUF, MASK>(j);
+    issue_v<1 - P>(j + 1);
+    if (j + 2 < n_tiles) issue_k<P>(j + 2);
+    rescale();
+    f32x16 sn[KB];
+    qk<1 - P>(sn);
+    uint32_t pk[KB][8], pl[KB][8];
+    softmax(scur, pk, pl);
+    pv<P>(pk, pl);
+    if (MASKN) mask(sn, (j + 1) * BN);
+    update_max(sn);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) scur[kb] = sn[kb];
     wait_all_and_barrier();
+  }
+
+  // The last tile (P = its index mod 2): nothing left to overlap.
+  template <int P>
+  __device__ __forceinline__ void last() {
+    rescale();
+    uint32_t pk[KB][8], pl[KB][8];
+    softmax(scur, pk, pl);
+    pv<P>(pk, pl);
   }
 
   __device__ __forceinline__ void run() {
@@ -256,10 +292,8 @@ struct FwdKernel {
     map_block(blockIdx.x, p.BH, p.n_qblocks, bh, qb);
     base = (size_t)bh * N * D;
     const uint16_t* Q = p.q + base;
-    K = p.k + base;
-    V = p.v + base;
-    krs = make_rsrc(K, N * D * 2);
-    vrs = make_rsrc(V, N * D * 2);
+    krs = make_rsrc(p.k + base, N * D * 2);
+    vrs = make_rsrc(p.v + base, N * D * 2);
     q0 = qb * BM;
     qw0 = q0 + 32 * w;
     myq = qw0 + (lane & 31);
@@ -274,41 +308,56 @@ struct FwdKernel {
       const int row = slot / CH, pchunk = slot % CH;
       voff[i] = (row * D + (pchunk ^ swz_pattern<CH>(row)) * 8) * 2;
     }
-    const int krow = sigma32(lane & 31);
-#pragma unroll
-    for (int c = 0; c < DC; ++c) kofs[c] = swz<CH>(krow, 2 * c + hi);
+    kbase = swz<CH>(sigma32(lane & 31), hi);
     const int g = lane >> 4, s = lane & 15;
     const int tr_row = 8 * (g >> 1) + (s >> 2);
     const int tr_col = 16 * (g & 1) + 4 * (s & 3);
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) vofs[hh][db] = swz_elem<CH>(tr_row + 4 * hh, 32 * db + tr_col);
+    vbase0 = swz_elem<CH>(tr_row, tr_col);
+    vbase1 = swz_elem<CH>(tr_row + 4, tr_col);
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
     Mraw = kNegInf;
     M2raw = kNegInf;
     m = kNegInf;
+    mb = 0.f;
     lsum = 0.f;
     flag = false;
 
     const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
     const int n_tiles = (kv_end + BN - 1) / BN;
-    issue_tile(0, 0);
-    wait_all_and_barrier();
-    // Leading tiles that need no mask for any wave of the workgroup (all keys
-    // before the first query, none past N) run unmasked, in pairs so that the
-    // buffer index stays a compile-time constant; the rest run masked.
+    // Tiles 0 .. n_plain-1 need no mask for any wave of the workgroup (all
+    // keys before the first query, none past N).
     const int n_plain = CAUSAL ? min(q0, N) / BN : N / BN;
+
+    // prologue: scores and maximum of tile 0
+    issue_k<0>(0);
+    issue_v<0>(0);
+    if (n_tiles > 1) issue_k<1>(1);
+    wait_all_and_barrier();
+    qk<0>(scur);
+    mask(scur, 0);
+    update_max(scur);
+
+    // steps 0 .. n_tiles-2, in pairs so that buffer indices are compile-time
+    // constants; a step masks the scores of its next tile unless that tile is
+    // one of the plain ones.
+    const int n_steps = n_tiles - 1;
+    const int n_plain_steps = min(n_plain - 1, n_steps);
     int j = 0;
-    for (; j + 2 <= n_plain; j += 2) {
+    for (; j + 2 <= n_plain_steps; j += 2) {
       step<0, false>(j, n_tiles);
       step<1, false>(j + 1, n_tiles);
     }
-    for (; j < n_tiles; j += 2) {
+    for (; j + 2 <= n_steps; j += 2) {
       step<0, true>(j, n_tiles);
-      if (j + 1 < n_tiles) step<1, true>(j + 1, n_tiles);
+      step<1, true>(j + 1, n_tiles);
     }
+    if (j < n_steps) {
+      step<0, true>(j, n_tiles);
+      ++j;
+    }
+    if (j & 1) last<1>();
+    else last<0>();
     epilogue();
   }
 
@@ -346,8 +395,12 @@ struct FwdKernel {
 
 template <int D, int MODE, bool CAUSAL, bool FLAGS>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * FwdKernel<D, MODE, CAUSAL, FLAGS>::TILE];
-  FwdKernel<D, MODE, CAUSAL, FLAGS> k(p, smem);
+  using Kt = FwdKernel<D, MODE, CAUSAL, FLAGS>;
+  __shared__ __attribute__((aligned(1024))) char k0[Kt::TILE];
+  __shared__ __attribute__((aligned(1024))) char k1[Kt::TILE];
+  __shared__ __attribute__((aligned(1024))) char v0[Kt::TILE];
+  __shared__ __attribute__((aligned(1024))) char v1[Kt::TILE];
+  Kt k(p, k0, k1, v0, v1);
   k.run();
 }
 
