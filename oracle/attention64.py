@@ -63,11 +63,15 @@ def fwd_slice(q, k, v, causal, scale):
 
 
 def bwd_slice(q, k, v, do, causal, scale, o=None):
-    """One slice of the backward.  Returns dict with dq, dk, dv, delta, delta_p.
+    """One slice of the backward.  Returns dict with dq, dk, dv, delta, delta_p,
+    cond_p, cond_o.
 
     delta uses O (the given one, or the exact O when o is None); delta_p is the
     equivalent rowsum(dP o P), which the pages report as the stabilising
-    alternative (section 3.4.2).
+    alternative (section 3.2 and section 3.4.2).  cond_p = rowsum(P o |dP|) and
+    cond_o = sum_i |dO_i| (P |V|)_i are the magnitudes the two sums are built
+    from: a computation of delta_p (or of rowsum(dO o P V)) with relative
+    rounding u per operation errs by a small multiple of u times them.
     """
     q = np.asarray(q, F64)
     k = np.asarray(k, F64)
@@ -79,10 +83,13 @@ def bwd_slice(q, k, v, do, causal, scale, o=None):
     dp = do @ v.T
     delta = np.sum(do * o_used, axis=-1)
     delta_p = np.sum(dp * p, axis=-1)
+    cond_p = np.sum(np.abs(dp) * p, axis=-1)
+    cond_o = np.sum(np.abs(do) * (p @ np.abs(v)), axis=-1)
     ds = p * (dp - delta[:, None])
     dq = F64(scale) * (ds @ k)
     dk = F64(scale) * (ds.T @ q)
-    return dict(dq=dq, dk=dk, dv=dv, delta=delta, delta_p=delta_p, p=p, o=o_exact)
+    return dict(dq=dq, dk=dk, dv=dv, delta=delta, delta_p=delta_p, cond_p=cond_p, cond_o=cond_o,
+                p=p, o=o_exact)
 
 
 def attention_fwd(q, k, v, causal=True, scale=None):
@@ -101,7 +108,8 @@ def attention_fwd(q, k, v, causal=True, scale=None):
 
 
 def attention_bwd(q, k, v, do, causal=True, scale=None, o=None):
-    """Batched backward.  Returns dict of float64 arrays dq, dk, dv, delta, delta_p.
+    """Batched backward.  Returns dict of float64 arrays dq, dk, dv, delta, delta_p,
+    cond_p, cond_o (see bwd_slice).
 
     o: optional output to form delta = rowsum(dO o O) with (e.g. the BF16 O of
     a kernel); by default the exact O is used.
@@ -113,7 +121,7 @@ def attention_bwd(q, k, v, do, causal=True, scale=None, o=None):
     n = q.shape[-2]
     rs = lambda x: None if x is None else np.asarray(x).reshape(nsl, x.shape[-2], x.shape[-1])
     qs, ks, vs, dos, os_ = rs(q), rs(k), rs(v), rs(do), rs(o)
-    out = {key: [] for key in ("dq", "dk", "dv", "delta", "delta_p")}
+    out = {key: [] for key in ("dq", "dk", "dv", "delta", "delta_p", "cond_p", "cond_o")}
     for i in range(nsl):
         r = bwd_slice(qs[i], ks[i], vs[i], dos[i], causal, scale,
                       None if os_ is None else os_[i])
@@ -141,7 +149,8 @@ def slice_reference(q, k, v, do=None, causal=True, scale=None, o_for_delta=None,
     are sums over query rows and are accumulated chunk by chunk.  Same
     definitions as fwd_slice / bwd_slice (pinned against them in the tests).
     o_for_delta: the O used in delta = rowsum(dO o O) (default: the exact O).
-    Returns dict(o, lse, dq, dk, dv, delta) of float64 arrays.
+    Returns dict(o, lse, dq, dk, dv, delta, delta_p, cond_p, cond_o) of float64
+    arrays (the last three as in bwd_slice).
     """
     q = np.asarray(q, F64)
     k = np.asarray(k, F64)
@@ -151,7 +160,8 @@ def slice_reference(q, k, v, do=None, causal=True, scale=None, o_for_delta=None,
     out = dict(o=np.empty((n, v.shape[1])), lse=np.empty(n))
     if do is not None:
         do = np.asarray(do, F64)
-        out.update(dq=np.empty((n, d)), dk=np.zeros_like(k), dv=np.zeros_like(v), delta=np.empty(n))
+        out.update(dq=np.empty((n, d)), dk=np.zeros_like(k), dv=np.zeros_like(v), delta=np.empty(n),
+                   delta_p=np.empty(n), cond_p=np.empty(n), cond_o=np.empty(n))
     for r0 in range(0, n, chunk):
         r1 = min(n, r0 + chunk)
         kend = r1 if causal else k.shape[0]
@@ -174,4 +184,7 @@ def slice_reference(q, k, v, do=None, causal=True, scale=None, o_for_delta=None,
         out["dk"][:kend] += F64(scale) * (ds.T @ q[r0:r1])
         out["dv"][:kend] += p.T @ g
         out["delta"][r0:r1] = delta
+        out["delta_p"][r0:r1] = np.sum(dp * p, axis=-1)
+        out["cond_p"][r0:r1] = np.sum(np.abs(dp) * p, axis=-1)
+        out["cond_o"][r0:r1] = np.sum(np.abs(g) * (p @ np.abs(v[:kend])), axis=-1)
     return out

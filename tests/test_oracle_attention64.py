@@ -104,6 +104,24 @@ def test_delta_identity():
     np.testing.assert_allclose(g["delta"], g["delta_p"], atol=1e-12)
 
 
+def test_delta_conditioning_bounds():
+    """cond_p and cond_o bound |delta_p| and |delta| (triangle inequality), and
+    reduce to the single product on a row with one visible key (causal row 0):
+    cond_p = |dO_0 . v_0|, cond_o = sum_i |dO_0i v_0i|."""
+    rng = np.random.default_rng(6)
+    n, d = 24, 8
+    q, k, v, do = (rng.standard_normal((n, d)) for _ in range(4))
+    g = a64.bwd_slice(q, k, v, do, True, 0.3)
+    assert np.all(np.abs(g["delta_p"]) <= g["cond_p"] * (1 + 1e-12))
+    assert np.all(np.abs(g["delta"]) <= g["cond_o"] * (1 + 1e-12))
+    assert np.isclose(g["cond_p"][0], abs(do[0] @ v[0]), rtol=1e-13)
+    assert np.isclose(g["cond_o"][0], np.sum(np.abs(do[0] * v[0])), rtol=1e-13)
+    # equal weights (zero queries): cond_o of the last row is the mean of |dO| . |v_t|
+    z = a64.bwd_slice(np.zeros((n, d)), k, v, do, True, 0.3)
+    want = np.mean(np.abs(v) @ np.abs(do[-1]))
+    assert np.isclose(z["cond_o"][-1], want, rtol=1e-13)
+
+
 def test_dq_error_identity():
     """dQ_hp - dQ_lp = scale * diag(delta_lp - delta_hp) (P K)  (section 3.4.3)."""
     rng = np.random.default_rng(5)
@@ -137,5 +155,5 @@ def test_row_chunked_reference_equals_whole_slice(causal):
     g = a64.bwd_slice(q, k, v, do, causal, 0.4)
     np.testing.assert_allclose(r["o"], o, atol=1e-13)
     np.testing.assert_allclose(r["lse"], lse, atol=1e-13)
-    for key in ("dq", "dk", "dv", "delta"):
+    for key in ("dq", "dk", "dv", "delta", "delta_p", "cond_p", "cond_o"):
         np.testing.assert_allclose(r[key], g[key], atol=1e-12)
