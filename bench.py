@@ -121,6 +121,31 @@ def run_mode(torch, pfa, inp, wl, mode, steps, warmup):
     return wall / steps * 1e3, avg_ms, ties
 
 
+def time_delta_sources(torch, pfa, inp, steps, warmup):
+    """Average duration of the backward's stage 1 with delta from rowsum(dP o P)
+    and from rowsum(dO o O_hp) (O recomputed in FP32), after a BF16 forward."""
+    dev = "cuda:0"
+    to = lambda x: torch.from_numpy(x).to(dev).to(torch.bfloat16).contiguous()
+    q, k, v, do = to(inp.q), to(inp.k), to(inp.v), to(inp.do_bf16)
+    B, H, N, d = q.shape
+    o, lse, _ = pfa.forward(q, k, v, causal=True, mode="bf16_out", flags=False)
+    ws = torch.empty(pfa.attn_bwd_workspace_bytes(B, H, N, d), device=dev, dtype=torch.uint8)
+    stream = torch.cuda.current_stream()
+    res = {}
+    for src in ("dp_p", "do_ohp"):
+        call = lambda: pfa.attn_bwd_delta(q, k, v, o, do, lse, ws, causal=True, delta_src=src, stream=stream)
+        for _ in range(warmup):
+            call()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[src] = round(e0.elapsed_time(e1) / steps, 4)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -130,6 +155,8 @@ def main():
     ap.add_argument("--workload", type=int, default=4, help="synthetic workload id (4 = long context)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-tie", action="store_true", help="skip the tie-aware mode timing")
+    ap.add_argument("--no-delta-sources", action="store_true",
+                    help="skip the timing of the alternative delta sources")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (for scaling the "
                          "HBM byte counters) and exit")
@@ -193,6 +220,12 @@ def main():
         extra["tie_aware_softmax"] = {"value": round(flops / (ms_t * 1e-3) / 1e12, 2),
                                       "ms_per_step": round(ms_t, 4),
                                       "phases_ms": {s: round(t, 4) for s, t in ph_t.items()}}
+
+    if not args.no_delta_sources:
+        # algorithmic work: S = QK^T and dP = dO V^T (dp_p), S and P V (do_ohp): 4 unit each
+        ds = time_delta_sources(torch, pfa, inp, args.steps, args.warmup)
+        extra["delta_sources"] = {src: {"ms": t, "tflops": round(4 * unit / (t * 1e-3) / 1e12, 2)}
+                                  for src, t in ds.items()}
 
     out = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),

@@ -154,6 +154,46 @@ int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout, c
                 const float* delta, void* dq, void* workspace, size_t workspace_bytes, int B, int H,
                 int N, int d, int causal, float scale, int mode, void* stream);
 
+/*
+ * Where the backward takes delta from: the isolation experiments of section
+ * 3.2 (and the error analysis of section 3.4.2) swap the standard term for
+ * equivalents that avoid the BF16 O of the forward.
+ *   PFA_DELTA_DO_O    rowsum(dO o O) with the stored O (the standard backward)
+ *   PFA_DELTA_DP_P    rowsum(dP o P), P = exp(S - LSE), dP = dO V^T with dO in
+ *                     BF16 (as the gradient kernels use it); FP32 products and
+ *                     sums.  Equal to the first in exact arithmetic.
+ *   PFA_DELTA_DO_OHP  rowsum(dO o O_hp): O = P V recomputed in the backward with
+ *                     FP32 accumulation, P split into BF16 hi + lo parts (both
+ *                     products on MFMA); dO as given (FP32 in PFA_FP32_OUT).
+ * The last two cost one more pass over the keys per query block.
+ */
+enum pfa_delta_src { PFA_DELTA_DO_O = 0, PFA_DELTA_DP_P = 1, PFA_DELTA_DO_OHP = 2 };
+
+/* Stage 1 with a choice of delta source: writes delta (into `delta`, or the
+ * workspace when NULL) and, in PFA_FP32_OUT, the BF16 copy of dO stages 2 and
+ * 3 read.  PFA_DELTA_DO_O is exactly attn_bwd_prep (q, k, v, lse unused and
+ * may be NULL); the other sources need q, k, v and lse.  Errors as
+ * attn_bwd_prep, plus PFA_ERR_INVALID for an unknown delta_src. */
+int attn_bwd_delta(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, float* delta, void* workspace, size_t workspace_bytes,
+                   int B, int H, int N, int d, int causal, float scale, int mode, int delta_src,
+                   void* stream);
+
+/* attn_bwd with delta taken from delta_src: attn_bwd_delta followed by
+ * stages 2 and 3.  With PFA_DELTA_DO_O it is attn_bwd. */
+int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                const float* lse, void* dq, void* dk, void* dv, float* delta, void* workspace,
+                size_t workspace_bytes, int B, int H, int N, int d, int causal, float scale,
+                int mode, int delta_src, void* stream);
+
+/* Diagnostic export of the error of delta (section 3.4.4): per row,
+ * err = rowsum(dO o O) - rowsum(dO o O_hp), the stored-O delta minus the
+ * PFA_DELTA_DO_OHP value, both with dO as given.  err: FP32 [B,H,N], device.
+ * Needs no workspace.  Errors as attn_fwd's argument checks. */
+int attn_delta_error(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                     const float* lse, float* err, int B, int H, int N, int d, int causal,
+                     float scale, int mode, void* stream);
+
 /* Static text for a status code. */
 const char* attn_strerror(int status);
 

@@ -6,8 +6,9 @@ output ("fp32_out") and the repeated-maximum-aware safe softmax
 ("tie_aware_softmax").  The kernels are hand-written HIP behind the C ABI in
 include/pfa_attn.h; this package is the thin Python binding.
 """
-from ._binding import (LIB_PATH, MODES, AttnError, attn_bwd, attn_bwd_dkdv,  # noqa: F401
-                       attn_bwd_dq, attn_bwd_prep, attn_bwd_workspace_bytes, attn_fwd,
-                       attn_strerror, backward, forward, lib)
+from ._binding import (DELTA_SRC, LIB_PATH, MODES, AttnError, attn_bwd,  # noqa: F401
+                       attn_bwd_delta, attn_bwd_dkdv, attn_bwd_dq, attn_bwd_prep,
+                       attn_bwd_workspace_bytes, attn_delta_error, attn_fwd, attn_strerror,
+                       backward, forward, lib)
 
 __version__ = "0.1.0"

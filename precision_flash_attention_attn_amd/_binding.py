@@ -16,8 +16,10 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "_lib", "libpfa_attn.so")
 
 MODES = {"bf16_out": 0, "fp32_out": 1, "tie_aware_softmax": 2}
+DELTA_SRC = {"do_o": 0, "dp_p": 1, "do_ohp": 2}
 PFA_OK, PFA_ERR_INVALID, PFA_ERR_UNSUPPORTED, PFA_ERR_HIP = 0, -1, -2, -3
 EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_prep", "attn_bwd_dkdv", "attn_bwd_dq",
+            "attn_bwd_delta", "attn_bwd_ex", "attn_delta_error",
             "attn_bwd_workspace_bytes", "attn_strerror", "attn_version")
 
 
@@ -57,6 +59,14 @@ def lib() -> ctypes.CDLL:
         L.attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                   i, i, i, i, i, f, i, vp]
         L.attn_bwd_dq.restype = i
+        L.attn_bwd_delta.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                     i, i, i, i, i, f, i, i, vp]
+        L.attn_bwd_delta.restype = i
+        L.attn_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                  i, i, i, i, i, f, i, i, vp]
+        L.attn_bwd_ex.restype = i
+        L.attn_delta_error.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+        L.attn_delta_error.restype = i
         L.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
         L.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.attn_strerror.argtypes = [i]
@@ -124,9 +134,18 @@ def attn_bwd_workspace_bytes(B, H, N, d, mode="bf16_out") -> int:
     return int(lib().attn_bwd_workspace_bytes(B, H, N, d, _mode_id(mode)))
 
 
+def _delta_src_id(src) -> int:
+    if isinstance(src, str):
+        if src not in DELTA_SRC:
+            raise ValueError(f"unknown delta source {src!r}")
+        return DELTA_SRC[src]
+    return int(src)
+
+
 def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, delta=None, causal=True, scale=None,
-             mode="bf16_out", stream=None):
-    """Backward pass into caller-allocated gradients (see attn_bwd in pfa_attn.h)."""
+             mode="bf16_out", stream=None, delta_src="do_o"):
+    """Backward pass into caller-allocated gradients (see attn_bwd and, for a
+    delta_src other than "do_o", attn_bwd_ex in pfa_attn.h)."""
     B, H, N, d = q.shape
     mid = _mode_id(mode)
     io = torch.float32 if mid == 1 else torch.bfloat16
@@ -141,9 +160,15 @@ def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, delta=None, causal=Tr
         raise ValueError("workspace: a contiguous GPU buffer is required")
     scale = 1.0 / d ** 0.5 if scale is None else float(scale)
     nbytes = workspace.numel() * workspace.element_size()
-    _check(lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
-                          _ptr(dk), _ptr(dv), _ptr(delta), _ptr(workspace), nbytes, B, H, N, d,
-                          int(bool(causal)), scale, mid, _stream(stream)))
+    src = _delta_src_id(delta_src)
+    if src == 0:
+        _check(lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                              _ptr(dk), _ptr(dv), _ptr(delta), _ptr(workspace), nbytes, B, H, N, d,
+                              int(bool(causal)), scale, mid, _stream(stream)))
+    else:
+        _check(lib().attn_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                                 _ptr(dk), _ptr(dv), _ptr(delta), _ptr(workspace), nbytes, B, H, N,
+                                 d, int(bool(causal)), scale, mid, src, _stream(stream)))
 
 
 def _ws(workspace):
@@ -164,6 +189,44 @@ def attn_bwd_prep(o, dout, workspace, delta=None, mode="bf16_out", stream=None):
     wp, wn = _ws(workspace)
     _check(lib().attn_bwd_prep(_ptr(o), _ptr(dout), _ptr(delta), wp, wn, B, H, N, d, mid,
                                _stream(stream)))
+
+
+def attn_bwd_delta(q, k, v, o, dout, lse, workspace, delta=None, causal=True, scale=None,
+                   mode="bf16_out", delta_src="do_o", stream=None):
+    """Backward stage 1 with a choice of delta source ("do_o", "dp_p", "do_ohp")."""
+    B, H, N, d = o.shape
+    mid = _mode_id(mode)
+    io = torch.float32 if mid == 1 else torch.bfloat16
+    _expect(o, "o", io, (B, H, N, d))
+    _expect(dout, "dout", io, (B, H, N, d))
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _expect(t, name, torch.bfloat16, (B, H, N, d))
+    _expect(lse, "lse", torch.float32, (B, H, N))
+    if delta is not None:
+        _expect(delta, "delta", torch.float32, (B, H, N))
+    scale = 1.0 / d ** 0.5 if scale is None else float(scale)
+    wp, wn = _ws(workspace)
+    _check(lib().attn_bwd_delta(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                                _ptr(delta), wp, wn, B, H, N, d, int(bool(causal)), scale, mid,
+                                _delta_src_id(delta_src), _stream(stream)))
+
+
+def attn_delta_error(q, k, v, o, dout, lse, err, causal=True, scale=None, mode="bf16_out",
+                     stream=None):
+    """err = rowsum(dO o O) - rowsum(dO o O_hp) per row (delta_lp - delta_hp)."""
+    B, H, N, d = o.shape
+    mid = _mode_id(mode)
+    io = torch.float32 if mid == 1 else torch.bfloat16
+    _expect(o, "o", io, (B, H, N, d))
+    _expect(dout, "dout", io, (B, H, N, d))
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _expect(t, name, torch.bfloat16, (B, H, N, d))
+    _expect(lse, "lse", torch.float32, (B, H, N))
+    _expect(err, "err", torch.float32, (B, H, N))
+    scale = 1.0 / d ** 0.5 if scale is None else float(scale)
+    _check(lib().attn_delta_error(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                                  _ptr(err), B, H, N, d, int(bool(causal)), scale, mid,
+                                  _stream(stream)))
 
 
 def _stage_args(q, k, v, dout, lse, delta, mode):
@@ -216,13 +279,16 @@ def forward(q, k, v, causal=True, scale=None, mode="bf16_out", beta=2.0, eps=1e-
     return o, lse, fl
 
 
-def backward(q, k, v, o, dout, lse, causal=True, scale=None, mode="bf16_out", want_delta=False):
-    """Allocate gradients and workspace and run attn_bwd.  Returns (dq, dk, dv, delta or None)."""
+def backward(q, k, v, o, dout, lse, causal=True, scale=None, mode="bf16_out", want_delta=False,
+             delta_src="do_o"):
+    """Allocate gradients and workspace and run attn_bwd (attn_bwd_ex for another
+    delta source).  Returns (dq, dk, dv, delta or None)."""
     B, H, N, d = q.shape
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
     ws = torch.empty(attn_bwd_workspace_bytes(B, H, N, d, mode), device=q.device, dtype=torch.uint8)
     delta = torch.empty((B, H, N), device=q.device, dtype=torch.float32) if want_delta else None
-    attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, ws, delta=delta, causal=causal, scale=scale, mode=mode)
+    attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, ws, delta=delta, causal=causal, scale=scale, mode=mode,
+             delta_src=delta_src)
     return dq, dk, dv, delta

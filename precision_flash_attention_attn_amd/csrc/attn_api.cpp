@@ -191,6 +191,90 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   return status_of(e);
 }
 
+int attn_bwd_delta(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, float* delta, void* workspace, size_t workspace_bytes, int B,
+                   int H, int N, int d, int causal, float scale, int mode, int delta_src,
+                   void* stream) {
+  if (delta_src != PFA_DELTA_DO_O && delta_src != PFA_DELTA_DP_P && delta_src != PFA_DELTA_DO_OHP)
+    return PFA_ERR_INVALID;
+  pfa::BwdArgs a;
+  const int st = bwd_args(a, workspace, workspace_bytes, delta, B, H, N, d, causal, scale, mode);
+  if (st != PFA_OK) return st;
+  if (!ok16(o) || !ok16(dout)) return PFA_ERR_INVALID;
+  if (delta_src != PFA_DELTA_DO_O) {
+    if (!ok16(q) || !ok16(k) || !ok16(v)) return PFA_ERR_INVALID;
+    if (!lse || !aligned4(lse)) return PFA_ERR_INVALID;
+  }
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  // the pre-pass also leaves the BF16 copy of dO that the FP32-output mode's
+  // gradient kernels read; its delta is then replaced
+  hipError_t e = hipSuccess;
+  if (delta_src == PFA_DELTA_DO_O || mode == PFA_FP32_OUT) e = pfa::launch_bwd_prep(a, s);
+  if (e == hipSuccess && delta_src != PFA_DELTA_DO_O) e = pfa::launch_bwd_delta(a, delta_src, a.delta, s);
+  return status_of(e);
+}
+
+int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                const float* lse, void* dq, void* dk, void* dv, float* delta, void* workspace,
+                size_t workspace_bytes, int B, int H, int N, int d, int causal, float scale,
+                int mode, int delta_src, void* stream) {
+  if (delta_src != PFA_DELTA_DO_O && delta_src != PFA_DELTA_DP_P && delta_src != PFA_DELTA_DO_OHP)
+    return PFA_ERR_INVALID;
+  pfa::BwdArgs a;
+  int st = bwd_args(a, workspace, workspace_bytes, delta, B, H, N, d, causal, scale, mode);
+  if (st != PFA_OK) return st;
+  if (!ok16(q) || !ok16(k) || !ok16(v) || !ok16(o) || !ok16(dout) || !ok16(dq) || !ok16(dk) ||
+      !ok16(dv))
+    return PFA_ERR_INVALID;
+  if (!lse || !aligned4(lse)) return PFA_ERR_INVALID;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (delta_src == PFA_DELTA_DO_O || mode == PFA_FP32_OUT) e = pfa::launch_bwd_prep(a, s);
+  if (e == hipSuccess && delta_src != PFA_DELTA_DO_O) e = pfa::launch_bwd_delta(a, delta_src, a.delta, s);
+  if (e == hipSuccess) e = pfa::launch_bwd_dkdv(a, s);
+  if (e == hipSuccess) e = pfa::launch_bwd_dq(a, s);
+  return status_of(e);
+}
+
+int attn_delta_error(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                     const float* lse, float* err, int B, int H, int N, int d, int causal,
+                     float scale, int mode, void* stream) {
+  const int st = check_common(B, H, N, d, scale, mode);
+  if (st != PFA_OK) return st;
+  if (!ok16(q) || !ok16(k) || !ok16(v) || !ok16(o) || !ok16(dout)) return PFA_ERR_INVALID;
+  if (!lse || !aligned4(lse) || !err || !aligned4(err)) return PFA_ERR_INVALID;
+  pfa::BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.d = d;
+  a.causal = causal ? 1 : 0;
+  a.mode = mode;
+  a.scale = scale;
+  return status_of(pfa::launch_bwd_delta(a, pfa::kDeltaErr, err, static_cast<hipStream_t>(stream)));
+}
+
 const char* attn_strerror(int status) {
   switch (status) {
     case PFA_OK: return "ok";

@@ -9,6 +9,9 @@ namespace pfa {
 
 enum Mode { kBf16Out = 0, kFp32Out = 1, kTieAware = 2 };
 
+// Sources of delta (the C ABI's pfa_delta_src), plus the error export.
+enum DeltaSrc { kDeltaDoO = 0, kDeltaDpP = 1, kDeltaOhp = 2, kDeltaErr = 3 };
+
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -54,5 +57,8 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
+// delta from another source (kDeltaDpP, kDeltaOhp) or delta_lp - delta_hp
+// (kDeltaErr), written to `out` [B,H,N].
+hipError_t launch_bwd_delta(const BwdArgs& a, int src, float* out, hipStream_t stream);
 
 }  // namespace pfa

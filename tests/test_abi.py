@@ -143,3 +143,26 @@ def test_backward_stages_reject_invalid_arguments(L):
     bad = list(dq_args)
     bad[12] = 48
     assert L.attn_bwd_dq(*bad) == uns
+
+
+def test_delta_entry_points_reject_invalid_arguments(L):
+    inv = bnd.PFA_ERR_INVALID
+    need = L.attn_bwd_workspace_bytes(1, 1, 128, 64, 0)
+    # attn_bwd_delta: unknown source, NULL q for a source that needs it, small workspace
+    args = lambda src, q=FAKE, ws_bytes=need, lse=FAKE: (q, FAKE, FAKE, FAKE, FAKE, lse, None, FAKE, ws_bytes,
+                                                           1, 1, 128, 64, 1, 0.125, 0, src, None)
+    assert L.attn_bwd_delta(*args(3)) == inv
+    assert L.attn_bwd_delta(*args(-1)) == inv
+    assert L.attn_bwd_delta(*args(1, q=None)) == inv
+    assert L.attn_bwd_delta(*args(2, lse=None)) == inv
+    assert L.attn_bwd_delta(*args(1, ws_bytes=need - 1)) == inv
+    # attn_bwd_ex: unknown source, misaligned output
+    ex = lambda src, dq=FAKE: (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, dq, FAKE, FAKE, None, FAKE, need,
+                               1, 1, 128, 64, 1, 0.125, 0, src, None)
+    assert L.attn_bwd_ex(*ex(7)) == inv
+    assert L.attn_bwd_ex(*ex(1, dq=FAKE + 2)) == inv
+    # attn_delta_error: NULL or misaligned err, bad mode
+    er = lambda err=FAKE, mode=0: (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, err, 1, 1, 128, 64, 1, 0.125, mode, None)
+    assert L.attn_delta_error(*er(err=None)) == inv
+    assert L.attn_delta_error(*er(err=FAKE + 2)) == inv
+    assert L.attn_delta_error(*er(mode=9)) == inv

@@ -77,9 +77,13 @@ def test_small_shapes_fwd_bwd(gpu, name, wl, causal, mode):
         for key in ("dq", "dk", "dv"):
             err = st.max_rel_err(g[key].reshape(B * H, N, d)[i], ref[key])
             assert err <= GRAD_TOL, (key, err)
-        # delta from the kernel's own O and dO, recomputed in float64
-        want = np.sum(do[i].astype(np.float64) * go[i], axis=-1)
-        assert st.max_rel_err(g["delta"].reshape(B * H, N)[i], want) <= 1e-5
+        # delta = rowsum(dO o O) against the oracle's with the emulator's O: the
+        # kernel's O differs from it by at most a couple of BF16 ulps (FP32: the
+        # last bits), so the bound is that much of sum |dO| |O|
+        want = np.sum(do[i].astype(np.float64) * emu.o[i], axis=-1)
+        mag = np.sum(np.abs(do[i]) * np.abs(emu.o[i]), axis=-1)
+        tol = (1e-5 if mode == "fp32_out" else 2.0 ** -7) * mag + 1e-30
+        assert np.all(np.abs(g["delta"].reshape(B * H, N)[i] - want) <= tol)
     mism, band = _flags_compare(g["flags"].reshape(B * H, N), emu)
     if band:
         print(f"  rows in the eps boundary band: {band}")
