@@ -99,6 +99,35 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int32_t* tie_flags, int B, int H, int N, int d, int causal, float scale,
              int mode, const pfa_tie_opts* opts, void* stream);
 
+/*
+ * attn_fwd plus a diagnostic: pbar_one (out, INT32 [B,H,N], device, required)
+ * counts per row the P-bar entries that round to 1 in BF16, i.e. exp(S - m) >=
+ * 1 - 2^-9.  In the BF16 modes these are exactly the P-bar = 1 additions at
+ * which the pages' cumulative error of O-bar jumps (section 3.4.4, "Why P-bar =
+ * 1 is the critical condition"); in PFA_FP32_OUT the same entries (there they
+ * enter as hi + lo, within 2^-9 of 1).  Same outputs as attn_fwd otherwise;
+ * runs a separate kernel variant, so attn_fwd pays nothing for it.
+ */
+int attn_fwd_diag(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int32_t* tie_flags, int32_t* pbar_one, int B, int H, int N, int d, int causal,
+                  float scale, int mode, const pfa_tie_opts* opts, void* stream);
+
+/*
+ * Forward with a mode per head: the pages' localisation experiment computes O
+ * in FP32 on selected heads only (section 3.2, "Failure is localized to
+ * specific attention heads"); the tie-aware softmax can be selected the same
+ * way.  head_modes: HOST array of H pfa_mode values.  o: FP32 [B,H,N,d] for
+ * every head -- heads in PFA_BF16_OUT or PFA_TIE_AWARE_SOFTMAX hold their BF16
+ * result widened exactly, so each head's O equals attn_fwd's in its own mode.
+ * lse, tie_flags, opts as attn_fwd.  The backward takes this O with mode
+ * PFA_FP32_OUT (dO FP32).  One kernel launch per mode present.  Errors as
+ * attn_fwd, plus PFA_ERR_INVALID for a NULL head_modes or an unknown mode in
+ * it, PFA_ERR_UNSUPPORTED for H > 256.
+ */
+int attn_fwd_heads(const void* q, const void* k, const void* v, float* o, float* lse,
+                   int32_t* tie_flags, int B, int H, int N, int d, int causal, float scale,
+                   const int32_t* head_modes, const pfa_tie_opts* opts, void* stream);
+
 /* Bytes of device workspace the backward needs: room for the FP32 delta row
  * vector [B,H,N] (used when the caller passes no delta buffer) and, in
  * PFA_FP32_OUT, a BF16 copy of dO for the MFMA operands; 256-byte aligned

@@ -19,7 +19,7 @@ MODES = {"bf16_out": 0, "fp32_out": 1, "tie_aware_softmax": 2}
 DELTA_SRC = {"do_o": 0, "dp_p": 1, "do_ohp": 2}
 PFA_OK, PFA_ERR_INVALID, PFA_ERR_UNSUPPORTED, PFA_ERR_HIP = 0, -1, -2, -3
 EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_prep", "attn_bwd_dkdv", "attn_bwd_dq",
-            "attn_bwd_delta", "attn_bwd_ex", "attn_delta_error",
+            "attn_bwd_delta", "attn_bwd_ex", "attn_delta_error", "attn_fwd_heads", "attn_fwd_diag",
             "attn_bwd_workspace_bytes", "attn_strerror", "attn_version")
 
 
@@ -67,6 +67,12 @@ def lib() -> ctypes.CDLL:
         L.attn_bwd_ex.restype = i
         L.attn_delta_error.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
         L.attn_delta_error.restype = i
+        L.attn_fwd_diag.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i,
+                                    ctypes.POINTER(TieOpts), vp]
+        L.attn_fwd_diag.restype = i
+        L.attn_fwd_heads.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp,
+                                     ctypes.POINTER(TieOpts), vp]
+        L.attn_fwd_heads.restype = i
         L.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
         L.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.attn_strerror.argtypes = [i]
@@ -128,6 +134,47 @@ def attn_fwd(q, k, v, o, lse, tie_flags=None, causal=True, scale=None, mode="bf1
     _check(lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(tie_flags),
                           B, H, N, d, int(bool(causal)), scale, mid, ctypes.byref(opts),
                           _stream(stream)))
+
+
+def attn_fwd_diag(q, k, v, o, lse, tie_flags, pbar_one, causal=True, scale=None, mode="bf16_out",
+                  beta=2.0, eps=1e-3, stream=None):
+    """attn_fwd plus the per-row count of P-bar entries equal to 1 (pbar_one, int32)."""
+    B, H, N, d = q.shape
+    mid = _mode_id(mode)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _expect(t, name, torch.bfloat16, (B, H, N, d))
+    _expect(o, "o", torch.float32 if mid == 1 else torch.bfloat16, (B, H, N, d))
+    _expect(lse, "lse", torch.float32, (B, H, N))
+    if tie_flags is not None:
+        _expect(tie_flags, "tie_flags", torch.int32, (B, H, N))
+    _expect(pbar_one, "pbar_one", torch.int32, (B, H, N))
+    scale = 1.0 / d ** 0.5 if scale is None else float(scale)
+    opts = TieOpts(float(beta), float(eps))
+    _check(lib().attn_fwd_diag(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(tie_flags),
+                               _ptr(pbar_one), B, H, N, d, int(bool(causal)), scale, mid,
+                               ctypes.byref(opts), _stream(stream)))
+
+
+def attn_fwd_heads(q, k, v, o, lse, head_modes, tie_flags=None, causal=True, scale=None,
+                   beta=2.0, eps=1e-3, stream=None):
+    """Forward with one mode per head (see attn_fwd_heads in pfa_attn.h); o is FP32."""
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _expect(t, name, torch.bfloat16, (B, H, N, d))
+    _expect(o, "o", torch.float32, (B, H, N, d))
+    _expect(lse, "lse", torch.float32, (B, H, N))
+    if tie_flags is not None:
+        _expect(tie_flags, "tie_flags", torch.int32, (B, H, N))
+    modes = [_mode_id(m) for m in head_modes]
+    if len(modes) != H:
+        raise ValueError(f"head_modes: expected {H} entries, got {len(modes)}")
+    arr = (ctypes.c_int32 * H)(*modes)
+    scale = 1.0 / d ** 0.5 if scale is None else float(scale)
+    opts = TieOpts(float(beta), float(eps))
+    _check(lib().attn_fwd_heads(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(tie_flags),
+                                B, H, N, d, int(bool(causal)), scale,
+                                ctypes.cast(arr, ctypes.c_void_p), ctypes.byref(opts),
+                                _stream(stream)))
 
 
 def attn_bwd_workspace_bytes(B, H, N, d, mode="bf16_out") -> int:
@@ -276,6 +323,16 @@ def forward(q, k, v, causal=True, scale=None, mode="bf16_out", beta=2.0, eps=1e-
     lse = torch.empty((B, H, N), device=q.device, dtype=torch.float32)
     fl = torch.empty((B, H, N), device=q.device, dtype=torch.int32) if flags else None
     attn_fwd(q, k, v, o, lse, fl, causal=causal, scale=scale, mode=mode, beta=beta, eps=eps)
+    return o, lse, fl
+
+
+def forward_heads(q, k, v, head_modes, causal=True, scale=None, beta=2.0, eps=1e-3, flags=True):
+    """Allocate outputs and run attn_fwd_heads.  Returns (o FP32, lse, tie_flags or None)."""
+    B, H, N, d = q.shape
+    o = torch.empty((B, H, N, d), device=q.device, dtype=torch.float32)
+    lse = torch.empty((B, H, N), device=q.device, dtype=torch.float32)
+    fl = torch.empty((B, H, N), device=q.device, dtype=torch.int32) if flags else None
+    attn_fwd_heads(q, k, v, o, lse, head_modes, fl, causal=causal, scale=scale, beta=beta, eps=eps)
     return o, lse, fl
 
 

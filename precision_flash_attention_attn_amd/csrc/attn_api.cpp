@@ -39,8 +39,10 @@ int check_common(int B, int H, int N, int d, float scale, int mode) {
 
 extern "C" {
 
-int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int32_t* tie_flags,
-             int B, int H, int N, int d, int causal, float scale, int mode,
+namespace {
+
+int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int32_t* tie_flags,
+             int32_t* pbar_one, int B, int H, int N, int d, int causal, float scale, int mode,
              const pfa_tie_opts* opts, void* stream) {
   int st = check_common(B, H, N, d, scale, mode);
   if (st != PFA_OK) return st;
@@ -72,8 +74,75 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   a.scale = scale;
   a.beta = beta;
   a.eps = eps;
+  a.pbar_one = pbar_one;
   const hipError_t e = pfa::launch_fwd(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PFA_OK : PFA_ERR_HIP;
+}
+
+}  // namespace
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int32_t* tie_flags,
+             int B, int H, int N, int d, int causal, float scale, int mode,
+             const pfa_tie_opts* opts, void* stream) {
+  return fwd_impl(q, k, v, o, lse, tie_flags, nullptr, B, H, N, d, causal, scale, mode, opts, stream);
+}
+
+int attn_fwd_diag(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int32_t* tie_flags, int32_t* pbar_one, int B, int H, int N, int d, int causal,
+                  float scale, int mode, const pfa_tie_opts* opts, void* stream) {
+  if (!pbar_one || !aligned4(pbar_one)) return PFA_ERR_INVALID;
+  return fwd_impl(q, k, v, o, lse, tie_flags, pbar_one, B, H, N, d, causal, scale, mode, opts, stream);
+}
+
+int attn_fwd_heads(const void* q, const void* k, const void* v, float* o, float* lse,
+                   int32_t* tie_flags, int B, int H, int N, int d, int causal, float scale,
+                   const int32_t* head_modes, const pfa_tie_opts* opts, void* stream) {
+  int st = check_common(B, H, N, d, scale, PFA_BF16_OUT);
+  if (st != PFA_OK) return st;
+  if (H > 256) return PFA_ERR_UNSUPPORTED;
+  if (!head_modes) return PFA_ERR_INVALID;
+  uint64_t masks[3][4] = {};
+  for (int h = 0; h < H; ++h) {
+    const int m = head_modes[h];
+    if (m != PFA_BF16_OUT && m != PFA_FP32_OUT && m != PFA_TIE_AWARE_SOFTMAX) return PFA_ERR_INVALID;
+    masks[m][h >> 6] |= uint64_t(1) << (h & 63);
+  }
+  if (!q || !k || !v || !o || !lse) return PFA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse))
+    return PFA_ERR_INVALID;
+  if (tie_flags && !aligned4(tie_flags)) return PFA_ERR_INVALID;
+  float beta = 2.0f, eps = 1e-3f;
+  if (opts) {
+    beta = opts->beta;
+    eps = opts->eps;
+  }
+  if (!std::isfinite(beta) || !(beta > 1.0f)) return PFA_ERR_INVALID;
+  if (!std::isfinite(eps) || !(eps >= 0.0f)) return PFA_ERR_INVALID;
+  for (int m = 0; m < 3; ++m) {
+    if (!(masks[m][0] | masks[m][1] | masks[m][2] | masks[m][3])) continue;
+    pfa::FwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.flags = tie_flags;
+    a.B = B;
+    a.H = H;
+    a.N = N;
+    a.d = d;
+    a.causal = causal ? 1 : 0;
+    a.mode = m;
+    a.scale = scale;
+    a.beta = beta;
+    a.eps = eps;
+    a.filter = 1;
+    a.o_f32 = 1;
+    for (int i = 0; i < 4; ++i) a.hmask[i] = masks[m][i];
+    const hipError_t e = pfa::launch_fwd(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return PFA_ERR_HIP;
+  }
+  return PFA_OK;
 }
 
 size_t attn_bwd_workspace_bytes(int B, int H, int N, int d, int mode) {

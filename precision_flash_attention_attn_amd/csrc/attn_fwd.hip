@@ -48,6 +48,12 @@ struct FwdParams {
   // literal infinity is folded back into fmaxf/fminf, which the compiler
   // surrounds with NaN-quieting copies of both operands)
   float pinf, ninf;
+  // Per-head selection: when `filter` is set, only heads h (of H) whose bit
+  // is set in hmask run; the others' workgroups exit at once.  o_f32: write
+  // O as FP32 (the BF16 result widened exactly in the BF16 modes).
+  int H, filter, o_f32;
+  uint64_t hmask[4];
+  int32_t* pbar_one;     // diagnostic variant: per-row count of P-bar entries equal to 1
 };
 
 // Row order of K inside a 32-key block: MFMA accumulator row i of lane half h
@@ -72,7 +78,14 @@ __device__ __forceinline__ void map_block(int bid, int BH, int nqb, int& bh, int
   }
 }
 
-template <int D, int MODE, bool CAUSAL, bool FLAGS>
+// DIAG (a diagnostic variant, always with FLAGS): also count, per row, the
+// P-bar entries that round to 1 in BF16 -- in the BF16 modes exactly the
+// P-bar = 1 additions the pages' cumulative-error trace singles out (section
+// 3.4.4, "Why P-bar = 1 is the critical condition").  In the FP32-output mode
+// the entries carry 1 - e (the exponent comes from one fma of the raw dot
+// product, whose rounding residue survives the hi + lo split) and the count is
+// of their BF16 hi part.
+template <int D, int MODE, bool CAUSAL, bool FLAGS, bool DIAG = false>
 struct FwdKernel {
   static constexpr int BM = 128, BN = 64, NT = 256;
   static constexpr int CH = D / 8;    // 16-byte chunks per K/V row
@@ -108,6 +121,7 @@ struct FwdKernel {
   f32x16 scur[KB];       // raw dot products of the tile whose P-bar is next
   float Mraw, M2raw, m, mb, alpha, lsum;
   bool flag;
+  int n_one;             // DIAG: this lane's count of P-bar == 1
 
   __device__ FwdKernel(const FwdParams& p_, char* k0, char* k1, char* v0, char* v1)
       : p(p_), kb0(k0), kb1(k1), vb0(v0), vb1(v1) {}
@@ -218,10 +232,16 @@ struct FwdKernel {
         const uint32_t u = pack_bf16(pa, pb);
         pk[kb][i] = u;
         lt = add_bf16_pair(u, lt);
+        uint32_t ul = 0;
         if (HP) {
-          const uint32_t ul = pack_bf16(pa - bf16lo_to_f32(u), pb - bf16hi_to_f32(u));
+          ul = pack_bf16(pa - bf16lo_to_f32(u), pb - bf16hi_to_f32(u));
           pl[kb][i] = ul;
           lt = add_bf16_pair(ul, lt);
+        }
+        if (DIAG) {
+          // P-bar rounds to BF16 1.0 (0x3f80); in the FP32-output mode this is the hi part
+          n_one += ((u & 0xffffu) == 0x3f80u) ? 1 : 0;
+          n_one += ((u >> 16) == 0x3f80u) ? 1 : 0;
         }
       }
     lsum = fmaf(lsum, alpha, lt);
@@ -290,6 +310,10 @@ struct FwdKernel {
     N = p.N;
     int qb;
     map_block(blockIdx.x, p.BH, p.n_qblocks, bh, qb);
+    if (p.filter) {
+      const int h = bh % p.H;
+      if (!((p.hmask[h >> 6] >> (h & 63)) & 1)) return;   // the whole workgroup: bh is uniform
+    }
     base = (size_t)bh * N * D;
     const uint16_t* Q = p.q + base;
     krs = make_rsrc(p.k + base, N * D * 2);
@@ -322,6 +346,7 @@ struct FwdKernel {
     mb = 0.f;
     lsum = 0.f;
     flag = false;
+    n_one = 0;
 
     const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
     const int n_tiles = (kv_end + BN - 1) / BN;
@@ -366,6 +391,12 @@ struct FwdKernel {
     float la, lb;
     pair32(lsum, la, lb);
     const float ltot = la + lb;
+    int ones = 0;
+    if (DIAG) {
+      float na, nb;
+      pair32(__int_as_float(n_one), na, nb);
+      ones = __float_as_int(na) + __float_as_int(nb);
+    }
     if (myq >= N) return;
     const size_t orow = base + (size_t)myq * D;
 #pragma unroll
@@ -382,20 +413,27 @@ struct FwdKernel {
           const float r0 = round_bf16(v0) / ltot, r1 = round_bf16(v1) / ltot;
           const float r2 = round_bf16(v2) / ltot, r3 = round_bf16(v3) / ltot;
           u32x2 out = {pack_bf16(r0, r1), pack_bf16(r2, r3)};
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.o) + orow + d0) = out;
+          if (p.o_f32) {
+            f32x4 wide = {bf16lo_to_f32(out.x), bf16hi_to_f32(out.x), bf16lo_to_f32(out.y),
+                          bf16hi_to_f32(out.y)};
+            *reinterpret_cast<f32x4*>(static_cast<float*>(p.o) + orow + d0) = wide;
+          } else {
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.o) + orow + d0) = out;
+          }
         }
       }
     }
     if (hi == 0) {
       p.lse[(size_t)bh * N + myq] = m + logf(ltot);
       if (FLAGS && p.flags) p.flags[(size_t)bh * N + myq] = flag ? 1 : 0;
+      if (DIAG) p.pbar_one[(size_t)bh * N + myq] = ones;
     }
   }
 };
 
-template <int D, int MODE, bool CAUSAL, bool FLAGS>
+template <int D, int MODE, bool CAUSAL, bool FLAGS, bool DIAG>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
-  using Kt = FwdKernel<D, MODE, CAUSAL, FLAGS>;
+  using Kt = FwdKernel<D, MODE, CAUSAL, FLAGS, DIAG>;
   __shared__ __attribute__((aligned(1024))) char k0[Kt::TILE];
   __shared__ __attribute__((aligned(1024))) char k1[Kt::TILE];
   __shared__ __attribute__((aligned(1024))) char v0[Kt::TILE];
@@ -404,7 +442,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   k.run();
 }
 
-template <int D, int MODE, bool CAUSAL, bool FLAGS>
+template <int D, int MODE, bool CAUSAL, bool FLAGS, bool DIAG = false>
 hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   FwdParams p;
   p.q = static_cast<const uint16_t*>(a.q);
@@ -421,8 +459,13 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   p.eps = a.eps;
   p.pinf = __builtin_inff();
   p.ninf = -__builtin_inff();
+  p.H = a.H;
+  p.filter = a.filter;
+  p.o_f32 = a.o_f32;
+  for (int i = 0; i < 4; ++i) p.hmask[i] = a.hmask[i];
+  p.pbar_one = a.pbar_one;
   const unsigned grid = (unsigned)(p.BH * p.n_qblocks);
-  hipLaunchKernelGGL((fwd_kernel<D, MODE, CAUSAL, FLAGS>), dim3(grid), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((fwd_kernel<D, MODE, CAUSAL, FLAGS, DIAG>), dim3(grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -431,6 +474,10 @@ hipError_t launch_m(const FwdArgs& a, hipStream_t stream) {
   // the tie-aware shift needs the running second maximum; the plain modes
   // track it only when the caller asks for the tie flags
   const bool flags = MODE == kTieAware || a.flags != nullptr;
+  if (a.pbar_one) {
+    if (a.causal) return launch_t<D, MODE, true, true, true>(a, stream);
+    return launch_t<D, MODE, false, true, true>(a, stream);
+  }
   if (a.causal) {
     if (flags) return launch_t<D, MODE, true, true>(a, stream);
     return launch_t<D, MODE, true, (MODE == kTieAware)>(a, stream);

@@ -23,6 +23,11 @@ struct FwdArgs {
   int causal;
   int mode;
   float scale, beta, eps;
+  // per-head selection (attn_fwd_heads): run only heads whose bit is set;
+  // o_f32: O is FP32 whatever the mode
+  int filter = 0, o_f32 = 0;
+  uint64_t hmask[4] = {0, 0, 0, 0};
+  int32_t* pbar_one = nullptr;   // attn_fwd_diag: per-row count of P-bar == 1
 };
 
 struct BwdArgs {

@@ -166,3 +166,25 @@ def test_delta_entry_points_reject_invalid_arguments(L):
     assert L.attn_delta_error(*er(err=None)) == inv
     assert L.attn_delta_error(*er(err=FAKE + 2)) == inv
     assert L.attn_delta_error(*er(mode=9)) == inv
+
+
+def test_per_head_forward_rejects_invalid_arguments(L):
+    inv, uns = bnd.PFA_ERR_INVALID, bnd.PFA_ERR_UNSUPPORTED
+    modes = (ctypes.c_int32 * 4)(0, 1, 2, 1)
+    bad = (ctypes.c_int32 * 4)(0, 1, 3, 1)
+    call = lambda hm, H=4, o=FAKE, d=64: L.attn_fwd_heads(FAKE, FAKE, FAKE, o, FAKE, None, 1, H, 128, d, 1,
+                                                          0.125, hm, None, None)
+    assert call(None) == inv
+    assert call(ctypes.cast(bad, ctypes.c_void_p)) == inv
+    assert call(ctypes.cast(modes, ctypes.c_void_p), o=FAKE + 4) == inv
+    assert call(ctypes.cast(modes, ctypes.c_void_p), d=80) == uns
+    many = (ctypes.c_int32 * 257)(*([0] * 257))
+    assert call(ctypes.cast(many, ctypes.c_void_p), H=257) == uns
+
+
+def test_diag_forward_requires_the_count_buffer(L):
+    inv = bnd.PFA_ERR_INVALID
+    f = lambda cnt: L.attn_fwd_diag(FAKE, FAKE, FAKE, FAKE, FAKE, None, cnt, 1, 1, 128, 64, 1, 0.125, 0,
+                                    None, None)
+    assert f(None) == inv
+    assert f(FAKE + 2) == inv
