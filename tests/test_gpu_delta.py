@@ -154,3 +154,17 @@ def test_delta_sources_long_context_one_head(gpu):
                               causal=True, scale=wl.scale)
     assert np.all(np.abs(g["dp_p"][0, 0] - ref["delta_p"]) <= 1e-4 * ref["cond_p"])
     assert np.all(np.abs(g["do_ohp"][0, 0] - ref["delta"]) <= 1e-4 * ref["cond_o"])
+
+
+def test_delta_sources_gpt2_small_shape(gpu):
+    """GPT-2-small layer shape (B8 H12 N1024 d64, low-rank keys, forced ties):
+    both alternative sources against the oracle on heads 0 and 11 of batch 0
+    and 7."""
+    wl = workload(2)
+    inp = generate(wl)
+    print("[delta] GPT-2-small shape", flush=True)
+    g = _deltas(gpu, inp, wl, "bf16_out", True)
+    for b, h in ((0, 0), (0, 11), (7, 0), (7, 11)):
+        ref = a64.bwd_slice(inp.q[b, h], inp.k[b, h], inp.v[b, h], inp.do_bf16[b, h], True, wl.scale)
+        assert np.all(np.abs(g["dp_p"][b, h] - ref["delta_p"]) <= 1e-4 * ref["cond_p"] + 1e-30)
+        assert np.all(np.abs(g["do_ohp"][b, h] - ref["delta"]) <= 1e-4 * ref["cond_o"] + 1e-30)

@@ -65,3 +65,25 @@ def test_pbar_one_count(gpu, name, wl, causal, mode):
     print(f"  rows with equal counts: {agree:.4f}; totals {got.sum()} vs {want.sum()}")
     assert agree >= 0.98
     assert abs(int(got.sum()) - int(want.sum())) <= 0.01 * want.sum() + 2
+
+
+def test_pbar_one_count_natural_ties(gpu):
+    """GPT-2-medium shape with natural ties only (B8 H16 N1024 d64, Q x4):
+    the counts of batch 0 against the emulator, head by head."""
+    import precision_flash_attention_attn_amd as pfa
+    wl = workload(3)
+    inp = generate(wl)
+    q, k, v = gpu.dev_bf16(inp.q), gpu.dev_bf16(inp.k), gpu.dev_bf16(inp.v)
+    B, H, N, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), device=q.device, dtype=torch.float32)
+    fl = torch.empty((B, H, N), device=q.device, dtype=torch.int32)
+    cnt = torch.empty_like(fl)
+    pfa.attn_fwd_diag(q, k, v, o, lse, fl, cnt)
+    torch.cuda.synchronize()
+    got = cnt[0].cpu().numpy()
+    emu = fe.flash_forward(inp.q[0], inp.k[0], inp.v[0], mode="bf16_out", causal=True, scale=wl.scale)
+    agree = np.mean(got == emu.n_pbar_one)
+    print(f"  rows with equal counts: {agree:.4f}; totals {got.sum()} vs {emu.n_pbar_one.sum()}")
+    assert agree >= 0.98
+    assert abs(int(got.sum()) - int(emu.n_pbar_one.sum())) <= 0.01 * emu.n_pbar_one.sum() + 2

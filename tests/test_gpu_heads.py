@@ -71,3 +71,44 @@ def test_per_head_modes(gpu, name, wl, causal, modes):
             for key, got in (("dq", gq[b, h]), ("dk", gk[b, h]), ("dv", gv[b, h])):
                 err = st.max_rel_err(got, ref[key])
                 assert err <= GRAD_TOL, (b, h, key, err)
+
+
+def test_per_head_modes_many_heads(gpu):
+    """130 heads (the head selection spans three 64-bit mask words): every
+    head's outputs equal the single-mode forward's for its mode, bit for bit."""
+    import precision_flash_attention_attn_amd as pfa
+    wl = Workload(83, "many_heads", 1, 130, 96, 64, tie_frac=0.1, tie_q_scale=8.0)
+    modes = [NAMES[(h * 7 + h // 3) % 3] for h in range(wl.h)]
+    print(f"[heads] 130 heads, mode counts { {m: modes.count(m) for m in NAMES} }", flush=True)
+    inp = generate(wl)
+    q, k, v = gpu.dev_bf16(inp.q), gpu.dev_bf16(inp.k), gpu.dev_bf16(inp.v)
+    o_h, lse_h, fl_h = pfa.forward_heads(q, k, v, modes)
+    single = {m: pfa.forward(q, k, v, mode=m) for m in NAMES}
+    torch.cuda.synchronize()
+    for h, m in enumerate(modes):
+        o_m, lse_m, fl_m = single[m]
+        assert torch.equal(o_h[:, h], o_m[:, h].float()), (h, m)
+        assert torch.equal(lse_h[:, h], lse_m[:, h]), (h, m)
+        assert torch.equal(fl_h[:, h], fl_m[:, h]), (h, m)
+
+
+def test_per_head_modes_fp32_stress_shape(gpu):
+    """The FP32-output stress shape (B2 H32 N4096 d128, Q x8): FP32 O on the
+    heads the pages single out in their localisation experiment (1, 7, 8, 9,
+    11, 12, counted from 1), BF16 elsewhere; bitwise equal to the single-mode
+    forwards, head by head."""
+    import precision_flash_attention_attn_amd as pfa
+    from synth.inputs import workload
+    wl = workload(5)
+    picked = {0, 6, 7, 8, 10, 11}
+    modes = ["fp32_out" if h in picked else "bf16_out" for h in range(wl.h)]
+    inp = generate(wl)
+    q, k, v = gpu.dev_bf16(inp.q), gpu.dev_bf16(inp.k), gpu.dev_bf16(inp.v)
+    o_h, lse_h, fl_h = pfa.forward_heads(q, k, v, modes)
+    single = {m: pfa.forward(q, k, v, mode=m) for m in ("bf16_out", "fp32_out")}
+    torch.cuda.synchronize()
+    for h, m in enumerate(modes):
+        o_m, lse_m, fl_m = single[m]
+        assert torch.equal(o_h[:, h], o_m[:, h].float()), (h, m)
+        assert torch.equal(lse_h[:, h], lse_m[:, h]), (h, m)
+        assert torch.equal(fl_h[:, h], fl_m[:, h]), (h, m)
