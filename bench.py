@@ -146,6 +146,36 @@ def time_delta_sources(torch, pfa, inp, steps, warmup):
     return res
 
 
+def signed_error_stats(torch, pfa, inp, wl):
+    """Mean signed O error on tied rows (rows whose tie flag is set), per mode,
+    against the FP32-output forward of the same inputs (accurate to ~1e-6
+    relative, far below the BF16 rounding measured here).  Two inputs: the
+    single-head tied-rows workload (B1 H1 N128 d64, 25% of rows with 2-4 tied
+    maxima and Q x8) pooled over 4096 seeded repetitions with V - 2 -- the
+    pages' mostly negative V, where plain BF16 is biased negative and the
+    tie-aware softmax removes most of it -- and the benchmarked workload itself
+    with V - 2 (there the tied keys carry a small share of each row's weight)."""
+    from synth.inputs import generate_reps, workload
+    dev = "cuda:0"
+    to = lambda x: torch.from_numpy(x).to(dev).to(torch.bfloat16).contiguous()
+    tied = generate_reps(workload(1), 4096)
+    out = {}
+    for name, x, shape in (("tied_rows_workload_x4096_v_minus_2", tied, "B4096 H1 N128 d64"),
+                           ("benchmarked_workload_v_minus_2", inp, f"B{wl.b} H{wl.h} N{wl.n} d{wl.d}")):
+        q, k, v = to(x.q), to(x.k), to(x.v - 2.0)
+        ref, _, fl = pfa.forward(q, k, v, causal=True, mode="fp32_out")
+        rows = fl.bool()
+        res = {"shape": shape, "tied_rows": int(rows.sum().item())}
+        for mode in ("bf16_out", "tie_aware_softmax"):
+            o, _, _ = pfa.forward(q, k, v, causal=True, mode=mode, flags=False)
+            err = (o.float() - ref)[rows]
+            res[mode] = {"mean_signed": float(err.mean().item()), "mean_abs": float(err.abs().mean().item())}
+        res["reduction"] = abs(res["bf16_out"]["mean_signed"]) / max(abs(res["tie_aware_softmax"]["mean_signed"]), 1e-30)
+        out[name] = res
+    torch.cuda.synchronize()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -157,6 +187,8 @@ def main():
     ap.add_argument("--no-tie", action="store_true", help="skip the tie-aware mode timing")
     ap.add_argument("--no-delta-sources", action="store_true",
                     help="skip the timing of the alternative delta sources")
+    ap.add_argument("--no-signed-error", action="store_true",
+                    help="skip the signed O error statistics on tied rows")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (for scaling the "
                          "HBM byte counters) and exit")
@@ -226,6 +258,9 @@ def main():
         ds = time_delta_sources(torch, pfa, inp, args.steps, args.warmup)
         extra["delta_sources"] = {src: {"ms": t, "tflops": round(4 * unit / (t * 1e-3) / 1e12, 2)}
                                   for src, t in ds.items()}
+
+    if not args.no_signed_error:
+        extra["signed_error_tied_rows"] = signed_error_stats(torch, pfa, inp, wl)
 
     out = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
