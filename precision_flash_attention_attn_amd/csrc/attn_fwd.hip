@@ -8,9 +8,10 @@
 // and the BF16 rounding of the FP32-accumulated product) and section 3.4.5
 // (the modified safe softmax inside the tiled forward pass).
 //
-// Work decomposition: one workgroup of 4 waves per (batch*head, block of 128
-// queries), two workgroups per CU; each wave owns 32 queries.  Keys stream in
-// tiles of 64 through a double-buffered LDS stage filled by direct
+// Work decomposition: one workgroup of 8 waves per (batch*head, block of 256
+// queries), one workgroup per CU (two waves per SIMD); each wave owns 32
+// queries, and every K/V tile staged in LDS serves all 256.  Keys stream in
+// tiles of 64 through double-buffered LDS stages filled by direct
 // global->LDS loads.  Per tile and wave:
 //   S^T (64 keys x 32 queries) = K_tile Q^T   (MFMA, A = K rows from LDS,
 //                                              B = the wave's Q held in VGPRs)
@@ -87,7 +88,7 @@ __device__ __forceinline__ void map_block(int bid, int BH, int nqb, int& bh, int
 // of their BF16 hi part.
 template <int D, int MODE, bool CAUSAL, bool FLAGS, bool DIAG = false>
 struct FwdKernel {
-  static constexpr int BM = 128, BN = 64, NT = 256;
+  static constexpr int BM = 256, BN = 64, NT = 512;
   static constexpr int CH = D / 8;    // 16-byte chunks per K/V row
   static constexpr int DC = D / 16;   // contraction steps of K Q^T
   static constexpr int KB = BN / 32;  // 32-key blocks per tile
@@ -432,7 +433,7 @@ struct FwdKernel {
 };
 
 template <int D, int MODE, bool CAUSAL, bool FLAGS, bool DIAG>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
   using Kt = FwdKernel<D, MODE, CAUSAL, FLAGS, DIAG>;
   __shared__ __attribute__((aligned(1024))) char k0[Kt::TILE];
   __shared__ __attribute__((aligned(1024))) char k1[Kt::TILE];
@@ -453,7 +454,7 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   p.flags = a.flags;
   p.BH = a.B * a.H;
   p.N = a.N;
-  p.n_qblocks = (a.N + 127) / 128;
+  p.n_qblocks = (a.N + FwdKernel<D, MODE, CAUSAL, FLAGS, DIAG>::BM - 1) / FwdKernel<D, MODE, CAUSAL, FLAGS, DIAG>::BM;
   p.scale = a.scale;
   p.beta = a.beta;
   p.eps = a.eps;
@@ -465,7 +466,7 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   for (int i = 0; i < 4; ++i) p.hmask[i] = a.hmask[i];
   p.pbar_one = a.pbar_one;
   const unsigned grid = (unsigned)(p.BH * p.n_qblocks);
-  hipLaunchKernelGGL((fwd_kernel<D, MODE, CAUSAL, FLAGS, DIAG>), dim3(grid), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((fwd_kernel<D, MODE, CAUSAL, FLAGS, DIAG>), dim3(grid), dim3(FwdKernel<D, MODE, CAUSAL, FLAGS, DIAG>::NT), 0, stream, p);
   return hipGetLastError();
 }
 
