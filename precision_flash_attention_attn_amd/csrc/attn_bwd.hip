@@ -189,11 +189,16 @@ struct DkdvKernel {
     asm volatile("" : "+v"(ab), "+v"(kbs), "+v"(t0), "+v"(t1));
     // S = Q K^T and dP = dO V^T; rows: queries (sigma order), columns: keys
     f32x16 sacc = f32x16{}, pacc = f32x16{};
+    // Wave priority 1 while the MFMA phases issue, 0 for the VALU phase: the
+    // other wave on the SIMD then fills the matrix core's gaps with its
+    // softmax work rather than competing with these products for issue.
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
       sacc = mfma_bf16(lds_read_b128(ql, ab ^ (32 * c)), lds_read_b128(kl, kbs ^ (32 * c)), sacc);
       pacc = mfma_bf16(lds_read_b128(dl, ab ^ (32 * c)), vreg[c], pacc);
     }
+    __builtin_amdgcn_s_setprio(0);
     // P = exp(S - LSE) and dS = P o (dP - delta), packed to BF16
     const float c1 = p.scale * kLog2e;
     uint32_t pP[8], pS[8];
@@ -224,6 +229,7 @@ struct DkdvKernel {
         pS[4 * hh + e / 2] = pack_bf16(ds[0], ds[1]);
       }
     }
+    __builtin_amdgcn_s_setprio(1);
     // dV^T += dO^T P, dK^T += Q^T dS over the half's 32 queries (two 16-query steps)
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
@@ -248,6 +254,7 @@ struct DkdvKernel {
   __device__ __forceinline__ void step(int t, int n_tiles) {
     if (t + 1 < n_tiles) issue_tile<1 - BUF>(qt_begin + (t + 1) * BQ);
     compute_tile<BUF, MASK>(qt_begin + t * BQ);
+    __builtin_amdgcn_s_setprio(0);
     wait_all_and_barrier();
   }
 
