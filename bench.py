@@ -187,6 +187,7 @@ def main():
     ap.add_argument("--no-tie", action="store_true", help="skip the tie-aware mode timing")
     ap.add_argument("--no-delta-sources", action="store_true",
                     help="skip the timing of the alternative delta sources")
+    ap.add_argument("--no-fp32", action="store_true", help="skip the fp32_out mode timing")
     ap.add_argument("--no-signed-error", action="store_true",
                     help="skip the signed O error statistics on tied rows")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -252,6 +253,13 @@ def main():
         extra["tie_aware_softmax"] = {"value": round(flops / (ms_t * 1e-3) / 1e12, 2),
                                       "ms_per_step": round(ms_t, 4),
                                       "phases_ms": {s: round(t, 4) for s, t in ph_t.items()}}
+    if not args.no_fp32 and args.mode != "fp32_out":
+        # the cost of the FP32-output remedy on the same workload: FP32 O and dO,
+        # the hi + lo P-bar operands (a second P-bar V product in the forward)
+        ms_f, ph_f, _ = run_mode(torch, pfa, inp, wl, "fp32_out", args.steps, args.warmup)
+        extra["fp32_out"] = {"value": round(flops / (ms_f * 1e-3) / 1e12, 2),
+                             "ms_per_step": round(ms_f, 4),
+                             "phases_ms": {s: round(t, 4) for s, t in ph_f.items()}}
 
     if not args.no_delta_sources:
         # algorithmic work: S = QK^T and dP = dO V^T (dp_p), S and P V (do_ohp): 4 unit each
