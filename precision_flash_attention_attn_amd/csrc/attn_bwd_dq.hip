@@ -72,9 +72,7 @@ struct DqKernel {
   char* sm1;
   int tid, lane, w, hi, N, bh, qw0, myq, q0;
   size_t base;
-  const uint16_t* K;
-  const uint16_t* V;
-  __amdgpu_buffer_rsrc_t krs, vrs;
+  __amdgpu_buffer_rsrc_t krs, vrs;   // this slice of K and V
   int voff[LOADS];
   int kofs[DC];
   int tofs[2][DB];
@@ -186,10 +184,8 @@ struct DqKernel {
     map_block(blockIdx.x, p.BH, p.n_qblocks, bh, qb);
     base = (size_t)bh * N * D;
     const uint16_t* Q = p.q + base;
-    K = p.k + base;
-    V = p.v + base;
-    krs = make_rsrc(K, N * D * 2);
-    vrs = make_rsrc(V, N * D * 2);
+    krs = make_rsrc(p.k + base, N * D * 2);
+    vrs = make_rsrc(p.v + base, N * D * 2);
     q0 = qb * BM;
     qw0 = q0 + 32 * w;
     myq = qw0 + (lane & 31);

@@ -168,3 +168,26 @@ def test_delta_sources_gpt2_small_shape(gpu):
         ref = a64.bwd_slice(inp.q[b, h], inp.k[b, h], inp.v[b, h], inp.do_bf16[b, h], True, wl.scale)
         assert np.all(np.abs(g["dp_p"][b, h] - ref["delta_p"]) <= 1e-4 * ref["cond_p"] + 1e-30)
         assert np.all(np.abs(g["do_ohp"][b, h] - ref["delta"]) <= 1e-4 * ref["cond_o"] + 1e-30)
+
+
+@pytest.mark.parametrize("mode", ["bf16_out", "fp32_out"])
+def test_delta_stage_then_gradient_stages_equal_one_call(gpu, mode):
+    """attn_bwd_delta followed by attn_bwd_dkdv and attn_bwd_dq on one stream
+    gives bit for bit what attn_bwd_ex gives (in the FP32-output mode the
+    delta stage also leaves the BF16 dO copy the gradient stages read)."""
+    import precision_flash_attention_attn_amd as pfa
+    name, wl, causal = CASES[2]
+    inp = generate(wl)
+    q, k, v = gpu.dev_bf16(inp.q), gpu.dev_bf16(inp.k), gpu.dev_bf16(inp.v)
+    o, lse, _ = pfa.forward(q, k, v, causal=causal, mode=mode)
+    do = gpu.dev_f32(inp.do_f32) if mode == "fp32_out" else gpu.dev_bf16(inp.do_bf16)
+    B, H, N, d = q.shape
+    for src in ("dp_p", "do_ohp"):
+        dq1, dk1, dv1, _ = pfa.backward(q, k, v, o, do, lse, causal=causal, mode=mode, delta_src=src)
+        ws = torch.empty(pfa.attn_bwd_workspace_bytes(B, H, N, d, mode), device=q.device, dtype=torch.uint8)
+        dq2, dk2, dv2 = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        pfa.attn_bwd_delta(q, k, v, o, do, lse, ws, causal=causal, mode=mode, delta_src=src)
+        pfa.attn_bwd_dkdv(q, k, v, do, lse, dk2, dv2, ws, causal=causal, mode=mode)
+        pfa.attn_bwd_dq(q, k, v, do, lse, dq2, ws, causal=causal, mode=mode)
+        torch.cuda.synchronize()
+        assert torch.equal(dq1, dq2) and torch.equal(dk1, dk2) and torch.equal(dv1, dv2), src
