@@ -9,8 +9,9 @@
 // (the modified safe softmax inside the tiled forward pass).
 //
 // Work decomposition: one workgroup of 8 waves per (batch*head, block of 256
-// queries), one workgroup per CU (two waves per SIMD); each wave owns 32
-// queries, and every K/V tile staged in LDS serves all 256.  Keys stream in
+// queries) at d = 128, one workgroup per CU (two waves per SIMD; at d = 64, 4
+// waves over 128 queries and two workgroups per CU); each wave owns 32
+// queries, and every K/V tile staged in LDS serves the whole block.  Keys stream in
 // tiles of 64 through double-buffered LDS stages filled by direct
 // global->LDS loads.  Per tile and wave:
 //   S^T (64 keys x 32 queries) = K_tile Q^T   (MFMA, A = K rows from LDS,
@@ -88,7 +89,11 @@ __device__ __forceinline__ void map_block(int bid, int BH, int nqb, int& bh, int
 // of their BF16 hi part.
 template <int D, int MODE, bool CAUSAL, bool FLAGS, bool DIAG = false>
 struct FwdKernel {
-  static constexpr int BM = 256, BN = 64, NT = 512;
+  // d = 128: 8 waves over 256 queries, one workgroup per CU; d = 64: 4 waves
+  // over 128 queries, two workgroups per CU (more, smaller workgroups balance
+  // the short sequences of the d = 64 shapes better).  Two waves per SIMD.
+  static constexpr int BM = D == 128 ? 256 : 128, BN = 64, NT = BM * 2;
+  static constexpr int MIN_WG = D == 128 ? 1 : 2;
   static constexpr int CH = D / 8;    // 16-byte chunks per K/V row
   static constexpr int DC = D / 16;   // contraction steps of K Q^T
   static constexpr int KB = BN / 32;  // 32-key blocks per tile
@@ -433,7 +438,8 @@ struct FwdKernel {
 };
 
 template <int D, int MODE, bool CAUSAL, bool FLAGS, bool DIAG>
-__global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__((FwdKernel<D, MODE, CAUSAL, FLAGS, DIAG>::NT),
+                             (FwdKernel<D, MODE, CAUSAL, FLAGS, DIAG>::MIN_WG)) void fwd_kernel(FwdParams p) {
   using Kt = FwdKernel<D, MODE, CAUSAL, FLAGS, DIAG>;
   __shared__ __attribute__((aligned(1024))) char k0[Kt::TILE];
   __shared__ __attribute__((aligned(1024))) char k1[Kt::TILE];
