@@ -9,8 +9,9 @@
 //   bwd_pre      delta = rowsum(dO o O) in FP32 (O, dO BF16, or FP32 in the
 //                FP32-output mode, where it also writes a BF16 copy of dO for
 //                the MFMA operands of the gradient kernels).
-//   bwd_dkdv     one workgroup of 8 waves per (batch*head, block of 128 keys);
-//                waves w and w + 4 own the same 32 keys and take the two
+//   bwd_dkdv     one workgroup per (batch*head, block of 128 keys at d = 128,
+//                64 at d = 64) of two waves per 32 keys; the two waves of a key
+//                group own the same 32 keys and take the two
 //                32-query halves of every query tile of 64 streaming through a
 //                double-buffered LDS stage; each accumulates partial dK^T, dV^T
 //                in MFMA accumulators, summed through LDS at the end:
@@ -104,7 +105,13 @@ __device__ __forceinline__ void map_kv_block(int bid, int BH, int& bh, int& kb) 
 
 template <int D, bool CAUSAL>
 struct DkdvKernel {
-  static constexpr int BKV = 128, BQ = 64, NT = 512;
+  // d = 128: 128 keys, 8 waves, one workgroup per CU; d = 64: 64 keys, 4
+  // waves, three workgroups per CU (the short sequences of the d = 64 shapes
+  // need the smaller blocks to fill the CUs).
+  static constexpr int BKV = D == 128 ? 128 : 64, BQ = 64;
+  static constexpr int KG = BKV / 32;                // key groups of 32
+  static constexpr int NT = 2 * KG * 64;
+  static constexpr int MIN_WG = D == 128 ? 1 : 3;
   static constexpr int CH = D / 8;
   static constexpr int DC = D / 16;
   static constexpr int DB = D / 32;
@@ -258,8 +265,8 @@ struct DkdvKernel {
     wait_all_and_barrier();
   }
 
-  // Sum the partial accumulators of waves w and w + 4 (same keys, other query
-  // half) through LDS and store the gradient from waves 0..3.  The exchange
+  // Sum the partial accumulators of waves w and w + KG (same keys, other query
+  // half) through LDS and store the gradient from waves 0..KG-1.  The exchange
   // area (DB x 16 floats x 64 lanes per key group) of key groups 0, 1 is in
   // buffer 0, of groups 2, 3 in buffer 1.
   __device__ __forceinline__ void reduce_store(f32x16* acc, uint16_t* out, float mul) {
@@ -295,8 +302,8 @@ struct DkdvKernel {
     lane = tid & 63;
     w = __builtin_amdgcn_readfirstlane(tid >> 6);
     hi = lane >> 5;
-    kb = w & 3;
-    qh = w >> 2;
+    kb = w % KG;
+    qh = w / KG;
     N = p.N;
     int kvb;
     map_kv_block(blockIdx.x, p.BH, bh, kvb);
@@ -373,7 +380,8 @@ struct DkdvKernel {
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(DkdvParams p) {
+__global__ __launch_bounds__((DkdvKernel<D, CAUSAL>::NT), (DkdvKernel<D, CAUSAL>::MIN_WG)) void bwd_dkdv_kernel(
+    DkdvParams p) {
   using Kt = DkdvKernel<D, CAUSAL>;
   constexpr int RED = 2 * (D / 32) * 4 * 64 * 16;   // exchange area of two key groups
   static_assert(RED <= Kt::BUFB, "the exchange area must fit one tile buffer");
@@ -411,11 +419,12 @@ hipError_t dkdv_d(const BwdArgs& a, hipStream_t stream) {
   p.dv = static_cast<uint16_t*>(a.dv);
   p.BH = a.B * a.H;
   p.N = a.N;
-  p.n_kvblocks = (a.N + 127) / 128;
+  using Kt = DkdvKernel<D, true>;
+  p.n_kvblocks = (a.N + Kt::BKV - 1) / Kt::BKV;
   p.scale = a.scale;
   const unsigned grid = (unsigned)(p.BH * p.n_kvblocks);
-  if (a.causal) hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(grid), dim3(512), 0, stream, p);
-  else hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(grid), dim3(512), 0, stream, p);
+  if (a.causal) hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(grid), dim3(Kt::NT), 0, stream, p);
+  else hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(grid), dim3(Kt::NT), 0, stream, p);
   return hipGetLastError();
 }
 
