@@ -77,7 +77,42 @@ def cpu_baseline(inp, wl, budget_s=12.0):
     flops = done * 7 * wl.n * wl.n * wl.d  # algorithmic FLOPs of the slices done (causal)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{done} of {nsl} (batch, head) slices, N={wl.n} d={wl.d}, causal, "
-                      f"float64 numpy forward+backward, {dt:.1f} s"}
+                      f"float64 numpy forward+backward, {dt:.1f} s",
+            "cpu_model": cpu_model(), "os_cpu_count": os.cpu_count()}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_emulator(inp, wl, mode, budget_s=4.0):
+    """The oracle's step-by-step BF16 flash emulator (a correctness tool, not
+    a baseline) on query rows of slice (0, 0): the tied rows first, then rows
+    spread over the sequence, in chunks of 64 until about budget_s seconds."""
+    import numpy as np
+    from oracle import flash_emu as fe
+    n = wl.n
+    tied = np.array(sorted({t for (b, h, t, _) in inp.forced_rows if b == 0 and h == 0}), dtype=int)
+    rest = np.setdiff1d(np.linspace(0, n - 1, 1024).astype(int), tied)
+    order = np.concatenate([tied, rest])
+    done = 0
+    t0 = time.perf_counter()
+    while done < len(order) and (time.perf_counter() - t0) < budget_s:
+        pos = order[done:done + 64]
+        fe.flash_forward(inp.q[0, 0][pos], inp.k[0, 0], inp.v[0, 0], mode=mode, causal=True,
+                         scale=wl.scale, q_pos=pos)
+        done += len(pos)
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "query rows/s", "kind": "emulator (correctness tool)",
+            "mode": mode, "sample": f"{done} query rows of slice (0, 0), N={n} d={wl.d}, causal "
+                                    f"({min(done, len(tied))} tied), {dt:.1f} s"}
 
 
 def run_mode(torch, pfa, inp, wl, mode, steps, warmup, candidates=("fwd", "bwd_dkdv", "bwd_dq")):
@@ -299,6 +334,7 @@ def main():
            "roofline": roofline}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, wl)
+        out["cpu_emulator"] = cpu_emulator(inp, wl, args.mode)
     out.update(extra)
     print(json.dumps(out), flush=True)
 
