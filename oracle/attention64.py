@@ -23,7 +23,8 @@ handled on its own so memory stays at a few N x N float64 matrices.
 Pinned by tests/test_oracle_attention64.py: brute-force scalar loops on tiny
 shapes, closed forms (zero queries give running means, row 0 of a causal
 product copies V[0]), softmax rows summing to one, central finite differences
-of sum(dO o O) for every gradient, the delta identity and the dQ identity.
+of sum(dO o O) for every gradient, the delta identity and the dQ identity;
+the row-chunked and row-sampled references against the whole-slice one.
 """
 from __future__ import annotations
 
@@ -187,4 +188,60 @@ def slice_reference(q, k, v, do=None, causal=True, scale=None, o_for_delta=None,
         out["delta_p"][r0:r1] = np.sum(dp * p, axis=-1)
         out["cond_p"][r0:r1] = np.sum(np.abs(dp) * p, axis=-1)
         out["cond_o"][r0:r1] = np.sum(np.abs(g) * (p @ np.abs(v[:kend])), axis=-1)
+    return out
+
+
+def sampled_reference(q, k, v, do, q_rows, k_rows, causal=True, scale=None, chunk=256):
+    """Forward and backward outputs of selected rows of one (batch, head)
+    slice in float64, for sequences too long for whole-slice references.
+
+    Query rows (O, LSE, delta, dQ) need only their own row of S.  A key row
+    j of dK = scale * dS^T Q and dV = P^T dO sums over every query i that sees
+    key j (i >= j when causal); each such query's row of P (and its delta) is
+    formed whole, `chunk` queries at a time, and only the columns of the
+    selected keys enter the sums.  Same definitions as fwd_slice / bwd_slice
+    (pinned against slice_reference in the tests).
+    Returns dict(o, lse, delta, dq) for q_rows and dict(dk, dv) for k_rows,
+    float64, in the order given.
+    """
+    q = np.asarray(q, F64)
+    k = np.asarray(k, F64)
+    v = np.asarray(v, F64)
+    do = np.asarray(do, F64)
+    n, d = q.shape
+    scale = F64(1.0 / np.sqrt(d) if scale is None else scale)
+    q_rows = np.asarray(q_rows, dtype=np.int64)
+    k_rows = np.asarray(k_rows, dtype=np.int64)
+    keys = np.arange(k.shape[0])
+
+    def rows_state(rows):
+        s = (q[rows] @ k.T) * scale
+        if causal:
+            s = np.where(keys[None, :] > rows[:, None], -np.inf, s)
+        p, lse = _softmax_rows(s)
+        o = p @ v
+        delta = np.sum(do[rows] * o, axis=-1)
+        return p, lse, o, delta
+
+    out = dict(o=np.empty((len(q_rows), v.shape[1])), lse=np.empty(len(q_rows)),
+               delta=np.empty(len(q_rows)), dq=np.empty((len(q_rows), d)),
+               dk=np.zeros((len(k_rows), d)), dv=np.zeros((len(k_rows), v.shape[1])))
+    for c0 in range(0, len(q_rows), chunk):
+        sel = slice(c0, min(len(q_rows), c0 + chunk))
+        rows = q_rows[sel]
+        p, lse, o, delta = rows_state(rows)
+        dp = do[rows] @ v.T
+        ds = p * (dp - delta[:, None])
+        out["o"][sel], out["lse"][sel], out["delta"][sel] = o, lse, delta
+        out["dq"][sel] = scale * (ds @ k)
+    if len(k_rows):
+        first = int(k_rows.min()) if causal else 0
+        for r0 in range(first, n, chunk):
+            rows = np.arange(r0, min(n, r0 + chunk))
+            p, _, _, delta = rows_state(rows)
+            pk = p[:, k_rows]
+            dpk = do[rows] @ v[k_rows].T
+            dsk = pk * (dpk - delta[:, None])
+            out["dk"] += scale * (dsk.T @ q[rows])
+            out["dv"] += pk.T @ do[rows]
     return out

@@ -182,6 +182,12 @@ struct FwdKernel {
   // products, then the S-unit maximum, tie flag and shift (section 3.4.5):
   // sets m, mb = m log2 e and alpha = exp(m_old - m) for the tile s.
   __device__ __forceinline__ void update_max(const f32x16 (&s)[KB]) {
+    // No contraction here: the compiler would otherwise fuse m - Mraw*scale
+    // (and Ms - M2raw*scale) into one fma with the unrounded product, so an
+    // unchanged maximum would give alpha = exp2(rounding residue) != 1 (and
+    // l and O-bar would drift by an ulp per tile), and the tie test would
+    // not use the rounded S values it is defined on.
+#pragma clang fp contract(off)
     const float hv = p.pinf, lv = p.ninf;
     float t1 = kNegInf, t2 = kNegInf;
 #pragma unroll

@@ -261,3 +261,77 @@ def test_backward_stages_equal_one_call(gpu, mode):
     h = gpu.host
     for a, b in ((dq1, dq2), (dk1, dk2), (dv1, dv2)):
         assert np.array_equal(h(a), h(b))
+
+
+LONG = [
+    ("n262144_d128_h2", Workload(96, "long sequence", 1, 2, 262144, 128, tie_frac=0.0005), MODES),
+    ("n262144_d64", Workload(97, "long sequence", 1, 1, 262144, 64, tie_frac=0.0005), ("bf16_out",)),
+]
+
+
+@pytest.mark.parametrize("name,wl,modes", LONG, ids=[c[0] for c in LONG])
+def test_long_sequence_sampled_rows(gpu, name, wl, modes):
+    """N = 2^18 (4096 key tiles per query row): sampled query rows (O, LSE,
+    dQ, tie flags; the first and last rows, tile edges, forced tied rows and
+    random rows) and sampled key rows of the last 1024 positions (dK, dV, each
+    a sum over every later query) against the float64 reference, per slice."""
+    inp = generate(wl)
+    B, H, N, d = wl.b, wl.h, wl.n, wl.d
+    rng = np.random.default_rng(wl.wid)
+    tied = [t for (b, h, t, _) in inp.forced_rows if b == 0 and h == 0][:8]
+    q_rows = np.unique(np.concatenate([[0, 1, 63, 64, 65, 255, 256, N // 2, N - 65, N - 64, N - 1],
+                                       tied, rng.integers(0, N, 40)]))
+    k_rows = np.unique(np.concatenate([[N - 1024, N - 513, N - 64, N - 1], rng.integers(N - 1024, N, 20)]))
+    q, k, v = (x.reshape(B * H, N, d) for x in (inp.q, inp.k, inp.v))
+    refs = {}
+    for mode in modes:
+        print(f"[long] {name} mode={mode}: {len(q_rows)} query rows, {len(k_rows)} key rows", flush=True)
+        g = gpu.run(inp, mode)
+        do = inp.do_for(mode).reshape(B * H, N, d)
+        for i in range(B * H):
+            kind = "f32" if mode == "fp32_out" else "bf16"
+            if (i, kind) not in refs:
+                refs[(i, kind)] = a64.sampled_reference(q[i], k[i], v[i], do[i], q_rows, k_rows,
+                                                        causal=True, scale=wl.scale)
+            ref = refs[(i, kind)]
+            sl = lambda key: g[key].reshape(B * H, N, -1)[i]
+            assert st.max_rel_err(sl("o")[q_rows], ref["o"]) <= TOL[mode]
+            # the BF16 modes sum the rounded P-bar into l: a row of a few keys errs by up to ~2^-9;
+            # the FP32-output pipeline keeps every step to a few FP32 roundings
+            lse_tol = 2e-5 if mode == "fp32_out" else 1e-2
+            assert np.max(np.abs(g["lse"].reshape(B * H, N)[i][q_rows] - ref["lse"])) <= lse_tol
+            for key, rows in (("dq", q_rows), ("dk", k_rows), ("dv", k_rows)):
+                err = st.max_rel_err(sl(key)[rows], ref[key])
+                assert err <= GRAD_TOL, (mode, i, key, err)
+            fl, _, gap, top = fe.tie_flags_untiled(q[i][q_rows], k[i], q_pos=q_rows, scale=wl.scale,
+                                                   return_gap=True)
+            band = np.abs(gap[0] - np.float32(1e-3)) <= 4 * f32_ulp(top[0])
+            gf = g["flags"].reshape(B * H, N)[i][q_rows]
+            assert np.array_equal(gf[~band], fl[0][~band])
+            print(f"  slice {i}: sampled tie rows gpu {int(gf.sum())} oracle {int(fl[0].sum())}", flush=True)
+
+
+def test_unchanged_maximum_leaves_the_sums_unscaled(gpu):
+    """A tile that does not raise a row's running maximum must rescale l and
+    O-bar by exactly 1.  Sharp rows (Q x4) of a 32768-key sequence raise their
+    maximum a handful of times over 512 tiles; a rescale factor one ulp above 1
+    on the other tiles would grow l by ~6e-5 and show in LSE, which the
+    FP32-output mode otherwise gets to a few FP32 roundings of the float64
+    value.  (An earlier kernel formed m - Mraw*scale as one fma with the
+    unrounded product and failed this by 2e-4.)"""
+    import precision_flash_attention_attn_amd as pfa
+    wl = Workload(98, "sharp long rows", 1, 1, 32768, 128, q_scale=4.0)
+    inp = generate(wl)
+    N = wl.n
+    rows = np.arange(N - 2048, N, 61)
+    ref = a64.sampled_reference(inp.q[0, 0], inp.k[0, 0], inp.v[0, 0], inp.do_f32[0, 0], rows,
+                                np.array([], dtype=np.int64), causal=True, scale=wl.scale)
+    q, k, v = (gpu.dev_bf16(x) for x in (inp.q, inp.k, inp.v))
+    o, lse, _ = pfa.forward(q, k, v, mode="fp32_out")
+    torch.cuda.synchronize()
+    err = gpu.host(lse)[0, 0][rows] - ref["lse"]
+    print(f"  lse error rms {np.sqrt(np.mean(err ** 2)):.2e} max {np.abs(err).max():.2e}", flush=True)
+    assert np.abs(err).max() <= 1e-5
+    o_rows = gpu.host(o)[0, 0][rows]
+    rel = np.linalg.norm(o_rows - ref["o"], axis=1) / np.linalg.norm(ref["o"], axis=1)
+    assert rel.max() <= 1e-4

@@ -157,3 +157,25 @@ def test_row_chunked_reference_equals_whole_slice(causal):
     np.testing.assert_allclose(r["lse"], lse, atol=1e-13)
     for key in ("dq", "dk", "dv", "delta", "delta_p", "cond_p", "cond_o"):
         np.testing.assert_allclose(r[key], g[key], atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_sampled_rows_equal_whole_slice(causal):
+    """The row-sampled reference (query rows for O, LSE, delta, dQ; key rows
+    for dK, dV, summed over every query that sees the key) equals the same
+    rows of the whole-slice reference; rows in arbitrary order, chunks that
+    split both loops."""
+    rng = np.random.default_rng(12)
+    n, d = 75, 8
+    q, k, v, do = (rng.standard_normal((n, d)) for _ in range(4))
+    qr = np.array([74, 0, 3, 40, 41, 1, 63])
+    kr = np.array([70, 5, 0, 74, 33])
+    r = a64.sampled_reference(q, k, v, do, qr, kr, causal=causal, scale=0.4, chunk=4)
+    o, lse, _ = a64.fwd_slice(q, k, v, causal, 0.4)
+    g = a64.bwd_slice(q, k, v, do, causal, 0.4)
+    np.testing.assert_allclose(r["o"], o[qr], atol=1e-13)
+    np.testing.assert_allclose(r["lse"], lse[qr], atol=1e-13)
+    np.testing.assert_allclose(r["delta"], g["delta"][qr], atol=1e-12)
+    np.testing.assert_allclose(r["dq"], g["dq"][qr], atol=1e-12)
+    np.testing.assert_allclose(r["dk"], g["dk"][kr], atol=1e-12)
+    np.testing.assert_allclose(r["dv"], g["dv"][kr], atol=1e-12)
