@@ -248,7 +248,7 @@ def main():
                          "HBM byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the (batch, head) slices would shard across GPUs with no exchange); run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
