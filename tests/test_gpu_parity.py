@@ -210,7 +210,8 @@ FULL = [
 @pytest.mark.parametrize("wid,modes,slices", FULL, ids=[f"cfg{c[0]}" for c in FULL])
 def test_full_size_configs(gpu, wid, modes, slices):
     """Full-size workloads in the benchmark's launch configuration; whole
-    (batch, head) slices are checked against the float64 reference."""
+    (batch, head) slices are checked against the float64 reference, and a
+    repeated run must give the same bits."""
     wl = workload(wid)
     inp = generate(wl)
     B, H, N, d = wl.b, wl.h, wl.n, wl.d
@@ -218,6 +219,10 @@ def test_full_size_configs(gpu, wid, modes, slices):
     for mode in modes:
         print(f"[full] cfg{wid} mode={mode}", flush=True)
         g = gpu.run(inp, mode)
+        # no atomics anywhere: a second run at full size gives the same bits
+        g2 = gpu.run(inp, mode)
+        for key in ("o", "lse", "flags", "dq", "dk", "dv", "delta"):
+            assert np.array_equal(g[key], g2[key]), (mode, key)
         do = inp.do_for(mode).reshape(B * H, N, d)
         for i in slices:
             ref = a64.slice_reference(q[i], k[i], v[i], do[i], causal=True, scale=wl.scale)
