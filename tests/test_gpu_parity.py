@@ -62,6 +62,42 @@ def _flags_compare(gpu_flags, emu):
 @pytest.mark.parametrize("name,wl,causal", SMALL, ids=[c[0] for c in SMALL])
 def test_small_shapes_fwd_bwd(gpu, name, wl, causal, mode):
     print(f"[parity] {name} mode={mode} shape={wl.b, wl.h, wl.n, wl.d} causal={causal}", flush=True)
+    _check_whole_slices(gpu, wl, causal, mode)
+
+
+def _random_shapes(count, seed):
+    """Seeded shapes around the tile edges (64-key tiles, 64/128/256-query blocks),
+    both head sizes, B*H from 1 to 15 (mostly not a multiple of 8), either mask,
+    modes in turn."""
+    rng = np.random.default_rng(seed)
+    lengths = [3, 17, 63, 64, 65, 127, 128, 129, 191, 255, 256, 257, 383, 511, 513]
+    out = []
+    for i in range(count):
+        n = int(rng.choice(lengths))
+        d = int(rng.choice([64, 128]))
+        b, h = int(rng.integers(1, 4)), int(rng.integers(1, 6))
+        causal = bool(rng.integers(0, 4) > 0)
+        mode = MODES[i % len(MODES)]
+        wl = Workload(200 + i, "random", b, h, n, d, tie_frac=0.05, tie_q_scale=float(rng.choice([1.0, 4.0, 8.0])))
+        out.append((f"r{i}_b{b}h{h}_n{n}_d{d}_{'c' if causal else 'nc'}_{mode}", wl, causal, mode))
+    return out
+
+
+RANDOM = _random_shapes(15, 31)
+
+
+@pytest.mark.parametrize("name,wl,causal,mode", RANDOM, ids=[c[0] for c in RANDOM])
+def test_random_shapes_fwd_bwd(gpu, name, wl, causal, mode):
+    """The checks of the small-shape test on seeded random shapes."""
+    print(f"[random] {name}", flush=True)
+    _check_whole_slices(gpu, wl, causal, mode)
+
+
+def _check_whole_slices(gpu, wl, causal, mode):
+    """Forward and backward of every (batch, head) slice against the float64
+    reference, delta against rowsum(dO o O) with the emulator's O, tie flags
+    against the emulator's (outside the eps boundary band) and O against the
+    BF16 emulator."""
     inp = generate(wl)
     g = gpu.run(inp, mode, causal=causal)
     B, H, N, d = wl.b, wl.h, wl.n, wl.d
