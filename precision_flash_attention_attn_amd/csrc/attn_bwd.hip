@@ -10,11 +10,12 @@
 //                FP32-output mode, where it also writes a BF16 copy of dO for
 //                the MFMA operands of the gradient kernels).
 //   bwd_dkdv     one workgroup per (batch*head, block of 128 keys at d = 128,
-//                64 at d = 64) of two waves per 32 keys; the two waves of a key
-//                group own the same 32 keys and take the two
-//                32-query halves of every query tile of 64 streaming through a
-//                double-buffered LDS stage; each accumulates partial dK^T, dV^T
-//                in MFMA accumulators, summed through LDS at the end:
+//                64 at d = 64); query tiles stream through a double-buffered
+//                LDS stage.  Split geometry: tiles of 64 queries, two waves per
+//                32 keys each take one 32-query half and accumulate partial
+//                dK^T, dV^T, summed through LDS at the end.  Unsplit geometry
+//                (d = 128 with B*H >= 32): tiles of 32 queries, one wave per 32
+//                keys, two workgroups per CU.  Per wave and tile:
 //                  S = Q K^T, dP = dO V^T          (A from LDS; B = K^T from the
 //                                                   key block in LDS, V^T in VGPRs)
 //                  P = exp(S - LSE), dS = P o (dP - delta)          (VALU)
@@ -103,15 +104,25 @@ __device__ __forceinline__ void map_kv_block(int bid, int BH, int& bh, int& kb) 
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPLIT>
 struct DkdvKernel {
   // d = 128: 128 keys, 8 waves, one workgroup per CU; d = 64: 64 keys, 4
   // waves, three workgroups per CU (the short sequences of the d = 64 shapes
   // need the smaller blocks to fill the CUs).
-  static constexpr int BKV = D == 128 ? 128 : 64, BQ = 64;
+  // Two geometries.  SPLIT: 64-query tiles, the two waves of a 32-key group
+  // take one half each and sum their partial gradients at the end (d = 128:
+  // 128 keys, 8 waves, one workgroup per CU; d = 64: 64 keys, 4 waves, three
+  // workgroups per CU -- the short sequences of the d = 64 shapes need the
+  // smaller blocks to fill the CUs).  Not SPLIT (d = 128 only): 32-query
+  // tiles, one wave per 32 keys takes the whole tile, two workgroups per CU,
+  // so the two waves on a SIMD belong to different workgroups and share no
+  // barrier.  The launcher picks the second when B*H >= 32 (measured: it is
+  // 2-11% faster there, 2-4% slower with 8 or 16 slices).
+  static_assert(SPLIT || D == 128, "the unsplit geometry is built for d = 128");
+  static constexpr int BKV = D == 128 ? 128 : 64, BQ = SPLIT ? 64 : 32;
   static constexpr int KG = BKV / 32;                // key groups of 32
-  static constexpr int NT = 2 * KG * 64;
-  static constexpr int MIN_WG = D == 128 ? 1 : 3;
+  static constexpr int NT = (SPLIT ? 2 : 1) * KG * 64;
+  static constexpr int MIN_WG = D == 128 ? (SPLIT ? 1 : 2) : 3;
   static constexpr int CH = D / 8;
   static constexpr int DC = D / 16;
   static constexpr int DB = D / 32;
@@ -156,7 +167,7 @@ struct DkdvKernel {
         buf2lds_b128(qrs, voff[i], qt0 * D * 2, dst);
         buf2lds_b128(dors, voff[i], qt0 * D * 2, dst + QT);
       }
-      if (w < 2)
+      if (w < 2 && lane < BQ)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(w == 0 ? lrs : drs,
                                                  (__attribute__((address_space(3))) void*)(bl + w * BQ * 4),
                                                  4, lane * 4, qt0 * 4, 0, 0);
@@ -170,7 +181,7 @@ struct DkdvKernel {
         buf2lds_b128(qrs, off, 0, dst);
         buf2lds_b128(dors, off, 0, dst + QT);
       }
-      if (w < 2)
+      if (w < 2 && lane < BQ)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(w == 0 ? lrs : drs,
                                                  (__attribute__((address_space(3))) void*)(bl + w * BQ * 4),
                                                  4, min(qt0 + lane, N - 1) * 4, 0, 0, 0);
@@ -270,6 +281,21 @@ struct DkdvKernel {
   // area (DB x 16 floats x 64 lanes per key group) of key groups 0, 1 is in
   // buffer 0, of groups 2, 3 in buffer 1.
   __device__ __forceinline__ void reduce_store(f32x16* acc, uint16_t* out, float mul) {
+    if constexpr (!SPLIT) {
+      if (mykey < N) {
+        const size_t krow = base + (size_t)mykey * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int d0 = 32 * db + 8 * j + 4 * hi;
+            const u32x2 v = {pack_bf16(mul * acc[db][4 * j], mul * acc[db][4 * j + 1]),
+                             pack_bf16(mul * acc[db][4 * j + 2], mul * acc[db][4 * j + 3])};
+            *reinterpret_cast<u32x2*>(out + krow + d0) = v;
+          }
+      }
+      return;
+    }
     f32x4* red = reinterpret_cast<f32x4*>(kb < 2 ? sm0 : sm1);
     const int kg = kb & 1;
     if (qh == 1) {
@@ -302,8 +328,8 @@ struct DkdvKernel {
     lane = tid & 63;
     w = __builtin_amdgcn_readfirstlane(tid >> 6);
     hi = lane >> 5;
-    kb = w % KG;
-    qh = w / KG;
+    kb = SPLIT ? w % KG : w;
+    qh = SPLIT ? w / KG : 0;
     N = p.N;
     int kvb;
     map_kv_block(blockIdx.x, p.BH, bh, kvb);
@@ -357,7 +383,8 @@ struct DkdvKernel {
     qt_begin = CAUSAL ? kv0 : 0;
     const int n_tiles = (N - qt_begin + BQ - 1) / BQ;
     const int n_full = (N - qt_begin) / BQ;
-    const int n_lead = CAUSAL ? min(2, n_tiles) : 0;
+    // tiles that overlap the key block need the causal mask: BKV / BQ of them (an even count)
+    const int n_lead = CAUSAL ? min(BKV / BQ < 2 ? 2 : BKV / BQ, n_tiles) : 0;
     if (n_tiles > 0) issue_tile<0>(qt_begin);
     wait_all_and_barrier();
     int t = 0;
@@ -379,12 +406,12 @@ struct DkdvKernel {
   }
 };
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__((DkdvKernel<D, CAUSAL>::NT), (DkdvKernel<D, CAUSAL>::MIN_WG)) void bwd_dkdv_kernel(
-    DkdvParams p) {
-  using Kt = DkdvKernel<D, CAUSAL>;
+template <int D, bool CAUSAL, bool SPLIT>
+__global__ __launch_bounds__((DkdvKernel<D, CAUSAL, SPLIT>::NT),
+                             (DkdvKernel<D, CAUSAL, SPLIT>::MIN_WG)) void bwd_dkdv_kernel(DkdvParams p) {
+  using Kt = DkdvKernel<D, CAUSAL, SPLIT>;
   constexpr int RED = 2 * (D / 32) * 4 * 64 * 16;   // exchange area of two key groups
-  static_assert(RED <= Kt::BUFB, "the exchange area must fit one tile buffer");
+  static_assert(!SPLIT || RED <= Kt::BUFB, "the exchange area must fit one tile buffer");
   __shared__ __attribute__((aligned(1024))) char kl[Kt::KBLK];
   __shared__ __attribute__((aligned(1024))) char s0[Kt::BUFB];
   __shared__ __attribute__((aligned(1024))) char s1[Kt::BUFB];
@@ -406,6 +433,16 @@ hipError_t prep_d(const BwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int D, bool SPLIT>
+hipError_t dkdv_launch(DkdvParams p, const BwdArgs& a, hipStream_t stream) {
+  using Kt = DkdvKernel<D, true, SPLIT>;
+  p.n_kvblocks = (a.N + Kt::BKV - 1) / Kt::BKV;
+  const unsigned grid = (unsigned)(p.BH * p.n_kvblocks);
+  if (a.causal) hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, SPLIT>), dim3(grid), dim3(Kt::NT), 0, stream, p);
+  else hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, SPLIT>), dim3(grid), dim3(Kt::NT), 0, stream, p);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t dkdv_d(const BwdArgs& a, hipStream_t stream) {
   DkdvParams p;
@@ -419,13 +456,10 @@ hipError_t dkdv_d(const BwdArgs& a, hipStream_t stream) {
   p.dv = static_cast<uint16_t*>(a.dv);
   p.BH = a.B * a.H;
   p.N = a.N;
-  using Kt = DkdvKernel<D, true>;
-  p.n_kvblocks = (a.N + Kt::BKV - 1) / Kt::BKV;
   p.scale = a.scale;
-  const unsigned grid = (unsigned)(p.BH * p.n_kvblocks);
-  if (a.causal) hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(grid), dim3(Kt::NT), 0, stream, p);
-  else hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(grid), dim3(Kt::NT), 0, stream, p);
-  return hipGetLastError();
+  if constexpr (D == 128)
+    if (p.BH >= 32) return dkdv_launch<D, false>(p, a, stream);
+  return dkdv_launch<D, true>(p, a, stream);
 }
 
 }  // namespace

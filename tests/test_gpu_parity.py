@@ -46,6 +46,9 @@ SMALL = [
     ("noncausal_n257_d128", Workload(94, "nc", 1, 3, 257, 128, tie_frac=0.05, tie_q_scale=8.0), False),
     ("noncausal_n190_d64", Workload(95, "nc64", 2, 2, 190, 64, tie_frac=0.05, tie_q_scale=8.0), False),
     ("bh8_n300_d64", Workload(96, "bh8", 2, 4, 300, 64, tie_frac=0.05, tie_q_scale=8.0), True),
+    # B*H >= 32 at d = 128: the dK/dV kernel's unsplit geometry (32-query tiles)
+    ("bh32_n333_d128", Workload(98, "bh32", 2, 16, 333, 128, tie_frac=0.05, tie_q_scale=4.0), True),
+    ("bh32_noncausal_n161_d128", Workload(99, "bh32nc", 4, 8, 161, 128, tie_frac=0.05, tie_q_scale=8.0), False),
 ]
 
 
