@@ -29,6 +29,8 @@ CASES = [
     ("ragged333_d64", Workload(90, "ragged", 1, 2, 333, 64, tie_frac=0.05, tie_q_scale=4.0), True),
     ("b2_n200_d128", Workload(91, "d128", 2, 1, 200, 128, tie_frac=0.05, tie_q_scale=4.0), True),
     ("noncausal_n257_d128", Workload(94, "nc", 1, 3, 257, 128, tie_frac=0.05, tie_q_scale=8.0), False),
+    # 32 (batch, head) slices at d = 128: the forward's 128-query geometry
+    ("bh32_n160_d128", Workload(95, "bh32", 2, 16, 160, 128, tie_frac=0.05, tie_q_scale=4.0), True),
 ]
 
 
