@@ -49,6 +49,8 @@ SMALL = [
     # B*H >= 32 at d = 128: the dK/dV kernel's unsplit geometry (32-query tiles)
     ("bh32_n333_d128", Workload(98, "bh32", 2, 16, 333, 128, tie_frac=0.05, tie_q_scale=4.0), True),
     ("bh32_noncausal_n161_d128", Workload(99, "bh32nc", 4, 8, 161, 128, tie_frac=0.05, tie_q_scale=8.0), False),
+    ("bh32_n1_d128", Workload(100, "bh32n1", 4, 8, 1, 128), True),
+    ("bh32_noncausal_n3_d128", Workload(101, "bh32n3", 2, 16, 3, 128), False),
 ]
 
 
