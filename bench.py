@@ -34,8 +34,11 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
 def source_hash() -> str:
+    """Hash of the device code (kernels and the headers they include): stored
+    counter readings stay valid while it is unchanged; host-side argument
+    checks do not enter it."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
+    for name in sorted(n for n in os.listdir(CSRC) if n.endswith((".hip", ".h"))):
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())

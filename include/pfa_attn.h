@@ -39,7 +39,8 @@
  *
  * Supported: d in {64, 128}; any N >= 1 (ragged tails are masked) with
  * N*d < 2^29 (byte offsets inside one (batch, head) slice stay 32-bit);
- * B, H >= 1; B*H*N*d < 2^40.
+ * B, H >= 1; B*H*N*d < 2^40; B*H*ceil(N/64) < 2^23 (the largest launch then
+ * stays under 2^32 threads).
  *
  * Errors: arguments are checked before anything is launched; a failed check
  * returns a negative status and writes nothing.  PFA_ERR_INVALID for a NULL

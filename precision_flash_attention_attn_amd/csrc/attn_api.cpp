@@ -18,8 +18,9 @@ int check_sizes(int B, int H, int N, int d) {
   if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return PFA_ERR_INVALID;
   const int64_t bh = int64_t(B) * H;
   if (bh * N * d >= kMaxElems) return PFA_ERR_INVALID;
-  // grid sizes: (B*H) * ceil(N/128) workgroups must fit a 31-bit grid
-  if (bh * ((int64_t(N) + 127) / 128) >= (int64_t(1) << 31)) return PFA_ERR_INVALID;
+  // launch sizes: the largest grid has (B*H) * ceil(N/64) workgroups of up to
+  // 512 threads, and a launch may hold fewer than 2^32 threads
+  if (bh * ((int64_t(N) + 63) / 64) >= (int64_t(1) << 23)) return PFA_ERR_INVALID;
   if (d != 64 && d != 128) return PFA_ERR_UNSUPPORTED;
   // tiles are staged with 32-bit byte offsets inside one (batch, head) slice
   if (int64_t(N) * d >= (int64_t(1) << 29)) return PFA_ERR_UNSUPPORTED;

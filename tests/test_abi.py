@@ -84,6 +84,9 @@ def test_fwd_rejects_invalid_arguments(L):
     assert _fwd(L, opts=bnd.TieOpts(2.0, -1e-3)) == inv
     assert _fwd(L, opts=bnd.TieOpts(2.0, float("nan"))) == inv
     assert _fwd(L, B=1 << 16, H=1 << 16, N=1 << 10, d=128) == inv   # too many elements
+    # launch size: B*H*ceil(N/64) < 2^23 (with up to 512 threads per workgroup)
+    assert _fwd(L, B=1 << 13, H=1 << 4, N=1 << 12, d=64) == inv     # 2^23 blocks of 64 keys
+    assert _fwd(L, B=1 << 13, H=1 << 4, N=(1 << 12) - 64, d=64, q=None) == inv   # accepted, then NULL q
     # one (batch, head) slice must keep 32-bit byte offsets: N*d < 2^29
     assert _fwd(L, N=1 << 22, d=128) == uns
     assert _fwd(L, N=(1 << 22) - 1, d=128, q=None) == inv   # size accepted, then the NULL q
