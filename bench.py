@@ -202,6 +202,38 @@ def time_delta_sources(torch, pfa, inp, steps, warmup):
     return res
 
 
+def tail_oriented_stats(torch, pfa, x, to, eps=1e-3):
+    """The signed O error on tied rows oriented by the tail, with V ~ N(0,1):
+    per element s = -sign(tau) (O_mode - O_ref), where tau is the part of the
+    row's unnormalised product that does not come from keys within eps of the
+    row maximum, sum over the other keys of exp(S - rm) V (float64).  Plain BF16
+    rounds the sum of the tied V values (P-bar = 1) against the small remainder,
+    so its s is negative; every step is odd in V, so for symmetric V the raw
+    mean is zero in expectation and only this orientation shows the bias.
+    Unit: the row (mean of s over its features); mean, standard error and
+    the plain / tie-aware ratio."""
+    q, k, v = to(x.q), to(x.k), to(x.v)
+    ref, _, fl = pfa.forward(q, k, v, causal=True, mode="fp32_out")
+    B, H, N, d = q.shape
+    s = torch.matmul(q.double(), k.double().transpose(-1, -2).contiguous()) * (1.0 / d ** 0.5)
+    s = s.masked_fill(torch.ones(N, N, dtype=torch.bool, device=q.device).triu(1), float("-inf"))
+    rm = s.amax(dim=-1, keepdim=True)
+    w = torch.exp(s - rm).masked_fill(s >= rm - eps, 0.0)
+    sign = torch.sign(torch.matmul(w, v.double()))
+    rows = fl.bool()
+    res = {"shape": f"B{B} H{H} N{N} d{d}", "v": "N(0,1)", "tied_rows": int(rows.sum().item())}
+    for mode in ("bf16_out", "tie_aware_softmax"):
+        o, _, _ = pfa.forward(q, k, v, causal=True, mode=mode, flags=False)
+        e = -sign * (o.double() - ref.double())
+        cnt = (sign != 0).double().sum(dim=-1)
+        per_row = (e.sum(dim=-1) / cnt.clamp(min=1))[rows & (cnt > 0)]
+        n = per_row.numel()
+        res[mode] = {"mean": float(per_row.mean().item()),
+                     "se": float(per_row.std().item() / n ** 0.5) if n > 1 else None}
+    res["reduction"] = abs(res["bf16_out"]["mean"]) / max(abs(res["tie_aware_softmax"]["mean"]), 1e-30)
+    return res
+
+
 def signed_error_stats(torch, pfa, inp, wl):
     """Mean signed O error on tied rows (rows whose tie flag is set), per mode,
     against the FP32-output forward of the same inputs (accurate to ~1e-6
@@ -210,12 +242,14 @@ def signed_error_stats(torch, pfa, inp, wl):
     maxima and Q x8) pooled over 4096 seeded repetitions with V - 2 -- the
     pages' mostly negative V, where plain BF16 is biased negative and the
     tie-aware softmax removes most of it -- and the benchmarked workload itself
-    with V - 2 (there the tied keys carry a small share of each row's weight)."""
+    with V - 2 (there the tied keys carry a small share of each row's weight);
+    and the tail-oriented statistic on the tied-rows workload with N(0,1) V
+    (tail_oriented_stats)."""
     from synth.inputs import generate_reps, workload
     dev = "cuda:0"
     to = lambda x: torch.from_numpy(x).to(dev).to(torch.bfloat16).contiguous()
     tied = generate_reps(workload(1), 4096)
-    out = {}
+    out = {"tied_rows_workload_x4096_tail_oriented": tail_oriented_stats(torch, pfa, tied, to)}
     for name, x, shape in (("tied_rows_workload_x4096_v_minus_2", tied, "B4096 H1 N128 d64"),
                            ("benchmarked_workload_v_minus_2", inp, f"B{wl.b} H{wl.h} N{wl.n} d{wl.d}")):
         q, k, v = to(x.q), to(x.k), to(x.v - 2.0)
