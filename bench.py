@@ -202,6 +202,18 @@ def time_delta_sources(torch, pfa, inp, steps, warmup):
     return res
 
 
+def tail_sums(torch, q, k, v, eps=1e-3):
+    """tau [B, H, N, d] in float64: for each query row of causal attention with
+    scale 1/sqrt(d), the sum over keys more than eps below the row's maximum
+    score of exp(S - rm) V (the keys within eps of the maximum are the tied ones)."""
+    N, d = q.shape[-2], q.shape[-1]
+    s = torch.matmul(q.double(), k.double().transpose(-1, -2).contiguous()) * (1.0 / d ** 0.5)
+    s = s.masked_fill(torch.ones(N, N, dtype=torch.bool, device=q.device).triu(1), float("-inf"))
+    rm = s.amax(dim=-1, keepdim=True)
+    w = torch.exp(s - rm).masked_fill(s >= rm - eps, 0.0)
+    return torch.matmul(w, v.double())
+
+
 def tail_oriented_stats(torch, pfa, x, to, eps=1e-3):
     """The signed O error on tied rows oriented by the tail, with V ~ N(0,1):
     per element s = -sign(tau) (O_mode - O_ref), where tau is the part of the
@@ -215,11 +227,7 @@ def tail_oriented_stats(torch, pfa, x, to, eps=1e-3):
     q, k, v = to(x.q), to(x.k), to(x.v)
     ref, _, fl = pfa.forward(q, k, v, causal=True, mode="fp32_out")
     B, H, N, d = q.shape
-    s = torch.matmul(q.double(), k.double().transpose(-1, -2).contiguous()) * (1.0 / d ** 0.5)
-    s = s.masked_fill(torch.ones(N, N, dtype=torch.bool, device=q.device).triu(1), float("-inf"))
-    rm = s.amax(dim=-1, keepdim=True)
-    w = torch.exp(s - rm).masked_fill(s >= rm - eps, 0.0)
-    sign = torch.sign(torch.matmul(w, v.double()))
+    sign = torch.sign(tail_sums(torch, q, k, v, eps))
     rows = fl.bool()
     res = {"shape": f"B{B} H{H} N{N} d{d}", "v": "N(0,1)", "tied_rows": int(rows.sum().item())}
     for mode in ("bf16_out", "tie_aware_softmax"):
