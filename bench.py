@@ -274,6 +274,68 @@ def signed_error_stats(torch, pfa, inp, wl):
     return out
 
 
+def signed_error_rows(torch, pfa, inp, mode, eps=1e-3):
+    """Mean signed O error of `mode` on the rows its tie flags mark, against the
+    FP32-output forward of the same inputs: raw, and oriented by the tail as in
+    tail_oriented_stats (tail sums one (batch, head) slice at a time).  The row
+    is the unit; returns mean and standard error of each, and the row count."""
+    dev = "cuda:0"
+    to = lambda x: torch.from_numpy(x).to(dev).to(torch.bfloat16).contiguous()
+    q, k, v = to(inp.q), to(inp.k), to(inp.v)
+    B, H, N, d = q.shape
+    ref, _, fl = pfa.forward(q, k, v, causal=True, mode="fp32_out")
+    o, _, _ = pfa.forward(q, k, v, causal=True, mode=mode, flags=False)
+    raw, tail = [], []
+    for b in range(B):
+        for h in range(H):
+            rows = fl[b, h].bool()
+            if not bool(rows.any()):
+                continue
+            sign = torch.sign(tail_sums(torch, q[b, h], k[b, h], v[b, h], eps))[rows]
+            e = (o[b, h].double() - ref[b, h].double())[rows]
+            raw.append(e.mean(dim=-1))
+            cnt = (sign != 0).double().sum(dim=-1)
+            keep = cnt > 0
+            tail.append(((-sign * e).sum(dim=-1) / cnt.clamp(min=1))[keep])
+    out = {"tied_rows": int(fl.sum().item())}
+    for name, xs in (("raw", raw), ("tail", tail)):
+        x = torch.cat(xs) if xs else torch.zeros(0, dtype=torch.float64, device=dev)
+        n = x.numel()
+        out[name] = {"mean": float(x.mean().item()) if n else None,
+                     "se": float(x.std().item() / n ** 0.5) if n > 1 else None}
+    return out
+
+
+def report(torch, pfa, steps, warmup):
+    """One JSON line per workload and mode (the five synthetic workloads, each
+    in the modes it lists): wall time of a fwd+bwd step (the four kernels,
+    inputs resident), TFLOP/s against the algorithmic count, tie rows, the
+    signed O error on tied rows (BF16 modes; the FP32-output forward is the
+    reference), and the float64 oracle's time on the host for the whole
+    workload, extrapolated from the slices it finishes in a few seconds."""
+    from synth.inputs import generate, workload
+    for wid in (1, 2, 3, 4, 5):
+        wl = workload(wid)
+        inp = generate(wl)
+        flops = wl.flops()
+        lines = []
+        for mode in wl.modes:
+            ms, phases, *_ , ties = run_mode(torch, pfa, inp, wl, mode, steps, warmup)
+            line = {"workload": wid, "name": wl.name, "shape": [wl.b, wl.h, wl.n, wl.d], "mode": mode,
+                    "ms_per_step": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+                    "pct_bf16_peak": round(100 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                    "phases_ms": {k_: round(v_, 4) for k_, v_ in phases.items()}, "tie_rows": ties}
+            if mode != "fp32_out":
+                line["signed_error"] = signed_error_rows(torch, pfa, inp, mode)
+            lines.append(line)
+        # the CPU leg after the GPU timings: seconds of an idle GPU lower its clocks
+        cpu = cpu_baseline(inp, wl, budget_s=4.0)
+        for line in lines:
+            line.update(cpu_float64_s=round(flops / (cpu["value"] * 1e12), 3), cpu_sample=cpu["sample"],
+                        cpu_cores=cpu["cores"])
+            print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -288,6 +350,9 @@ def main():
     ap.add_argument("--no-fp32", action="store_true", help="skip the fp32_out mode timing")
     ap.add_argument("--no-signed-error", action="store_true",
                     help="skip the signed O error statistics on tied rows")
+    ap.add_argument("--report", action="store_true",
+                    help="instead of the benchmark line, one JSON line per workload (1-5) and mode: "
+                         "fwd+bwd time, TFLOP/s, tie rows, signed O error on tied rows, CPU float64 time")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (for scaling the "
                          "HBM byte counters) and exit")
@@ -318,6 +383,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     pfa.lib()  # fail loudly if the HIP library is missing
+    if args.report:
+        report(torch, pfa, args.steps, args.warmup)
+        return
     wl = workload(args.workload)
     inp = generate(wl)
     flops = wl.flops()

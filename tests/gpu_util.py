@@ -2,6 +2,9 @@
 the C ABI (via the thin binding), results back to numpy."""
 from __future__ import annotations
 
+import json
+import os
+
 import numpy as np
 import torch
 
@@ -35,3 +38,18 @@ def run(inp, mode, causal=True, scale=None, bwd=True, beta=2.0, eps=1e-3):
         out.update(dq=host(dq), dk=host(dk), dv=host(dv), delta=host(delta))
     torch.cuda.synchronize()
     return out
+
+
+def record(section: str, key: str, value) -> None:
+    """Add a measured figure to the JSON file named by PFA_PARITY_REPORT (if
+    set): {section: {key: value}}, merged with what is already there."""
+    path = os.environ.get("PFA_PARITY_REPORT")
+    if not path:
+        return
+    data = {}
+    if os.path.exists(path):
+        with open(path) as f:
+            data = json.load(f)
+    data.setdefault(section, {})[key] = value
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)

@@ -67,7 +67,9 @@ def _flags_compare(gpu_flags, emu):
 @pytest.mark.parametrize("name,wl,causal", SMALL, ids=[c[0] for c in SMALL])
 def test_small_shapes_fwd_bwd(gpu, name, wl, causal, mode):
     print(f"[parity] {name} mode={mode} shape={wl.b, wl.h, wl.n, wl.d} causal={causal}", flush=True)
-    _check_whole_slices(gpu, wl, causal, mode)
+    rec = _check_whole_slices(gpu, wl, causal, mode)
+    if name == "cfg1":
+        gpu.record("full_size", f"cfg1_{mode}", rec)
 
 
 def _random_shapes(count, seed):
@@ -110,13 +112,16 @@ def _check_whole_slices(gpu, wl, causal, mode):
     do = inp.do_for(mode).reshape(B * H, N, d)
     go = g["o"].reshape(B * H, N, d)
     emu = fe.flash_forward(q, k, v, mode=mode, causal=causal, scale=wl.scale)
+    rec = {"slices": "all", "o": 0.0, "dq": 0.0, "dk": 0.0, "dv": 0.0}
     for i in range(B * H):
         ref = a64.slice_reference(q[i], k[i], v[i], do[i], causal=causal, scale=wl.scale)
+        rec["o"] = max(rec["o"], st.max_rel_err(go[i], ref["o"]))
         assert st.max_rel_err(go[i], ref["o"]) <= TOL[mode]
         lse_tol = 1e-4 if mode == "fp32_out" else 1e-2
         assert np.max(np.abs(g["lse"].reshape(B * H, N)[i] - ref["lse"])) <= lse_tol
         for key in ("dq", "dk", "dv"):
             err = st.max_rel_err(g[key].reshape(B * H, N, d)[i], ref[key])
+            rec[key] = max(rec[key], err)
             assert err <= GRAD_TOL, (key, err)
         # delta = rowsum(dO o O) against the oracle's with the emulator's O: the
         # kernel's O differs from it by at most a couple of BF16 ulps (FP32: the
@@ -129,6 +134,8 @@ def _check_whole_slices(gpu, wl, causal, mode):
     if band:
         print(f"  rows in the eps boundary band: {band}")
     assert mism == 0
+    rec["tie_rows_gpu"] = int(g["flags"].sum())
+    rec["tie_rows_oracle"] = int(emu.flag.sum())
     if mode == "fp32_out":
         # FP32 output: the accumulation order differs from the emulator's in the last bits only
         assert st.max_rel_err(go, emu.o) <= 1e-5
@@ -137,6 +144,7 @@ def _check_whole_slices(gpu, wl, causal, mode):
         agree = np.mean(go == emu.o)
         print(f"  O bitwise agreement with the BF16 emulator: {agree:.4f}")
         assert agree >= 0.9
+    return rec
 
 
 def _within_one_bf16_ulp(a, b, ulps=1):
@@ -234,6 +242,8 @@ def test_signed_error_gate_config1(gpu):
         fl = g["flags"].reshape(b, 128)
         res[mode] = st.signed_error(g["o"].reshape(b, 128, 64), o64, tau, fl)
         print(f"[signed error] {mode}: {res[mode]}", flush=True)
+        gpu.record("signed_error_cfg1_x4096", mode,
+                   {k_: float(v_) for k_, v_ in res[mode].items() if np.isscalar(v_)})
     p, t, f = res["bf16_out"], res["tie_aware_softmax"], res["fp32_out"]
     assert p["tail_mean"] < -5 * p["tail_se"]
     assert abs(t["tail_mean"]) * 10 <= abs(p["tail_mean"])
@@ -265,12 +275,16 @@ def test_full_size_configs(gpu, wid, modes, slices):
         for key in ("o", "lse", "flags", "dq", "dk", "dv", "delta"):
             assert np.array_equal(g[key], g2[key]), (mode, key)
         do = inp.do_for(mode).reshape(B * H, N, d)
+        rec = {"slices": list(slices), "o": 0.0, "dq": 0.0, "dk": 0.0, "dv": 0.0,
+               "tie_rows_gpu": 0, "tie_rows_oracle": 0, "tie_rows_all_slices_gpu": int(g["flags"].sum())}
         for i in slices:
             ref = a64.slice_reference(q[i], k[i], v[i], do[i], causal=True, scale=wl.scale)
             go = g["o"].reshape(B * H, N, d)[i]
+            rec["o"] = max(rec["o"], st.max_rel_err(go, ref["o"]))
             assert st.max_rel_err(go, ref["o"]) <= TOL[mode]
             for key in ("dq", "dk", "dv"):
                 err = st.max_rel_err(g[key].reshape(B * H, N, d)[i], ref[key])
+                rec[key] = max(rec[key], err)
                 assert err <= GRAD_TOL, (key, err)
             fl_ref = np.zeros(N, bool)
             band = np.zeros(N, bool)
@@ -284,6 +298,9 @@ def test_full_size_configs(gpu, wid, modes, slices):
             print(f"  slice {i}: tie rows gpu {int(gf.sum())} oracle {int(fl_ref.sum())} "
                   f"boundary rows {int(band.sum())}", flush=True)
             assert np.array_equal(gf[~band], fl_ref[~band])
+            rec["tie_rows_gpu"] += int(gf.sum())
+            rec["tie_rows_oracle"] += int(fl_ref.sum())
+        gpu.record("full_size", f"cfg{wid}_{mode}", rec)
 
 
 @pytest.mark.parametrize("mode", MODES)
