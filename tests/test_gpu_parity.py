@@ -201,6 +201,27 @@ def test_never_fired_rows_match_plain_bitwise(gpu):
     assert np.array_equal(p["flags"], t["flags"])
 
 
+@pytest.mark.parametrize("mode", MODES)
+def test_tie_flag_one_ulp_either_side_of_eps(gpu, mode):
+    """Exact inputs whose top-two score gap is fp32(eps) -/+ one ulp: the GPU
+    flags the first row and not the second, and every row's flag equals the
+    oracle's (no boundary band: the scores are exact); in the tie-aware mode
+    the flagged row's output follows the emulator's shifted softmax."""
+    from eps_boundary import T, boundary_inputs
+    q, k, v, expect = boundary_inputs()
+    inp = type("Inputs", (), {})()
+    inp.q, inp.k, inp.v = q, k, v
+    g = gpu.run(inp, mode, scale=0.125, bwd=False)
+    for h in range(2):
+        fl, _ = fe.tie_flags_untiled(q[0, h], k[0, h], scale=0.125)
+        assert bool(g["flags"][0, h, T]) == expect[h], (h, mode)
+        assert np.array_equal(g["flags"][0, h], fl[0]), (h, mode)
+        emu = fe.flash_forward(q[0, h][None], k[0, h][None], v[0, h][None], mode=mode, causal=True,
+                               scale=0.125)
+        tol = 1e-5 if mode == "fp32_out" else 2.0 ** -7
+        assert np.all(np.abs(g["o"][0, h] - emu.o[0]) <= tol * np.maximum(np.abs(emu.o[0]), 1.0)), (h, mode)
+
+
 def test_tie_shift_underflow_gives_nan_rows(gpu):
     """A tied row with (beta - 1) * rm beyond the FP32 exp range has l = 0 and
     NaN output; untied rows are unaffected."""

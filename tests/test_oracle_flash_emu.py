@@ -214,3 +214,20 @@ def test_sign_claim_negative_values_paper_condition():
     p, t = res["bf16_out"], res["tie_aware_softmax"]
     assert p["raw_mean"] < -5 * p["raw_se"]
     assert abs(t["raw_mean"]) < 0.5 * abs(p["raw_mean"])
+
+
+def test_flag_one_ulp_either_side_of_eps():
+    """Exact inputs whose top-two score gap is fp32(eps) -/+ one ulp (2^-33):
+    the untiled rule and the tiled emulator (one tile, and 2-key tiles whose
+    running top two meet across tiles) flag the first and not the second."""
+    from eps_boundary import T, boundary_inputs
+    q, k, v, expect = boundary_inputs()
+    for h in range(2):
+        fl, _, gap, _ = fe.tie_flags_untiled(q[0, h], k[0, h], scale=0.125, return_gap=True)
+        assert gap[0][T] == np.float64(np.float32(1e-3)) + (-1 if h == 0 else 1) * 2.0 ** -33
+        assert bool(fl[0][T]) == expect[h]
+        for bn in (64, 2):
+            r = fe.flash_forward(q[0, h][None], k[0, h][None], v[0, h][None], mode="tie_aware_softmax",
+                                 causal=True, scale=0.125, bn=bn)
+            assert bool(r.flag[0][T]) == expect[h]
+            assert np.array_equal(r.flag[0], fl[0])
