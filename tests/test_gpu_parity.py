@@ -222,6 +222,38 @@ def test_tie_flag_one_ulp_either_side_of_eps(gpu, mode):
         assert np.all(np.abs(g["o"][0, h] - emu.o[0]) <= tol * np.maximum(np.abs(emu.o[0]), 1.0)), (h, mode)
 
 
+TIE_PARAMS = [(4.0, 1e-3), (8.0, 1e-3), (2.0, 1e-2), (2.0, 1e-4), (1.5, 0.0)]
+
+
+@pytest.mark.parametrize("beta,eps", TIE_PARAMS, ids=[f"beta{b}_eps{e}" for b, e in TIE_PARAMS])
+def test_tie_parameters(gpu, beta, eps):
+    """The tie-aware softmax at other shift factors (the pages recommend beta in
+    [2, 8]) and tie thresholds: flags equal the emulator's outside the eps
+    boundary band, O agrees with the emulator and with the float64 attention
+    (the shift leaves the exact result unchanged), gradients as usual."""
+    wl = Workload(130, "tie params", 1, 2, 300, 64, tie_frac=0.1, tie_q_scale=2.0)
+    inp = generate(wl)
+    mode = "tie_aware_softmax"
+    g = gpu.run(inp, mode, beta=beta, eps=eps)
+    B, H, N, d = wl.b, wl.h, wl.n, wl.d
+    q, k, v = (x.reshape(B * H, N, d) for x in (inp.q, inp.k, inp.v))
+    do = inp.do_for(mode).reshape(B * H, N, d)
+    emu = fe.flash_forward(q, k, v, mode=mode, causal=True, scale=wl.scale, beta=beta, eps=eps)
+    gap = emu.row_max - emu.row_max2
+    with np.errstate(invalid="ignore"):
+        band = np.isfinite(gap) & (np.abs(gap - np.float32(eps)) <= 4 * f32_ulp(emu.row_max))
+    gf = g["flags"].reshape(B * H, N)
+    assert np.array_equal(gf[~band], emu.flag[~band])
+    assert gf.sum() > 0 and np.all(np.isfinite(g["o"]))
+    go = g["o"].reshape(B * H, N, d)
+    assert np.mean(go == emu.o) >= 0.9
+    for i in range(B * H):
+        ref = a64.slice_reference(q[i], k[i], v[i], do[i], causal=True, scale=wl.scale)
+        assert st.max_rel_err(go[i], ref["o"]) <= TOL[mode]
+        for key in ("dq", "dk", "dv"):
+            assert st.max_rel_err(g[key].reshape(B * H, N, d)[i], ref[key]) <= GRAD_TOL, key
+
+
 def test_tie_shift_underflow_gives_nan_rows(gpu):
     """A tied row with (beta - 1) * rm beyond the FP32 exp range has l = 0 and
     NaN output; untied rows are unaffected."""
