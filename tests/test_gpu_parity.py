@@ -222,6 +222,30 @@ def test_tie_flag_one_ulp_either_side_of_eps(gpu, mode):
         assert np.all(np.abs(g["o"][0, h] - emu.o[0]) <= tol * np.maximum(np.abs(emu.o[0]), 1.0)), (h, mode)
 
 
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("scale", (0.1, 0.3))
+def test_other_scales(gpu, scale, mode):
+    """A softmax scale other than 1/sqrt(d), not a power of two: the kernels keep
+    raw dot products and scale only the row's top two for the tie test, which
+    must equal the test on S = fp32(fp32(q.k) * scale) (rounding is monotone).
+    Flags against the emulator outside the eps band, outputs and gradients
+    against float64."""
+    wl = Workload(131, "scale", 1, 2, 257, 128, tie_frac=0.1, tie_q_scale=2.0)
+    inp = generate(wl)
+    g = gpu.run(inp, mode, scale=scale)
+    B, H, N, d = wl.b, wl.h, wl.n, wl.d
+    q, k, v = (x.reshape(B * H, N, d) for x in (inp.q, inp.k, inp.v))
+    do = inp.do_for(mode).reshape(B * H, N, d)
+    emu = fe.flash_forward(q, k, v, mode=mode, causal=True, scale=scale)
+    mism, _ = _flags_compare(g["flags"].reshape(B * H, N), emu)
+    assert mism == 0 and g["flags"].sum() > 0
+    for i in range(B * H):
+        ref = a64.slice_reference(q[i], k[i], v[i], do[i], causal=True, scale=scale)
+        assert st.max_rel_err(g["o"].reshape(B * H, N, d)[i], ref["o"]) <= TOL[mode]
+        for key in ("dq", "dk", "dv"):
+            assert st.max_rel_err(g[key].reshape(B * H, N, d)[i], ref[key]) <= GRAD_TOL, key
+
+
 TIE_PARAMS = [(4.0, 1e-3), (8.0, 1e-3), (2.0, 1e-2), (2.0, 1e-4), (1.5, 0.0)]
 
 
