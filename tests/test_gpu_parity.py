@@ -383,29 +383,34 @@ def test_full_size_configs(gpu, wid, modes, slices):
 RAGGED_LARGE = [
     # B*H >= 32: 128-query forward, unsplit dK/dV (32-query tiles); ragged by 3
     ("bh32_n4099_d128", Workload(120, "ragged large", 2, 16, 4099, 128, tie_frac=0.01, tie_q_scale=4.0),
-     (0, 31), "bf16_out"),
+     (0, 31), "bf16_out", True),
     # B*H < 32: 256-query forward, split dK/dV; one key short of a tile edge
     ("bh2_n8191_d128", Workload(121, "ragged large", 1, 2, 8191, 128, tie_frac=0.01), (0, 1),
-     "tie_aware_softmax"),
+     "tie_aware_softmax", True),
     ("bh3_n2113_d64", Workload(122, "ragged large", 1, 3, 2113, 64, tie_frac=0.01, tie_q_scale=8.0), (0, 2),
-     "fp32_out"),
+     "fp32_out", True),
+    # without the causal mask: every tile is plain but the ragged last one
+    ("noncausal_bh32_n3001_d128", Workload(123, "ragged large", 4, 8, 3001, 128, tie_frac=0.01,
+                                           tie_q_scale=4.0), (0, 31), "tie_aware_softmax", False),
+    ("noncausal_bh2_n5000_d64", Workload(124, "ragged large", 2, 1, 5000, 64, tie_frac=0.01), (0, 1),
+     "bf16_out", False),
 ]
 
 
-@pytest.mark.parametrize("name,wl,slices,mode", RAGGED_LARGE, ids=[c[0] for c in RAGGED_LARGE])
-def test_ragged_large_shapes(gpu, name, wl, slices, mode):
+@pytest.mark.parametrize("name,wl,slices,mode,causal", RAGGED_LARGE, ids=[c[0] for c in RAGGED_LARGE])
+def test_ragged_large_shapes(gpu, name, wl, slices, mode, causal):
     """Sequence lengths thousands of keys long that end inside a tile, in the
-    launch geometries of the large workloads: whole (batch, head) slices of O,
-    LSE, dQ, dK, dV against the float64 reference, tie flags against the
-    untiled rule."""
-    print(f"[ragged large] {name} mode={mode}", flush=True)
+    launch geometries of the large workloads, with and without the causal
+    mask: whole (batch, head) slices of O, LSE, dQ, dK, dV against the float64
+    reference, tie flags against the untiled rule."""
+    print(f"[ragged large] {name} mode={mode} causal={causal}", flush=True)
     inp = generate(wl)
     B, H, N, d = wl.b, wl.h, wl.n, wl.d
-    g = gpu.run(inp, mode)
+    g = gpu.run(inp, mode, causal=causal)
     q, k, v = (x.reshape(B * H, N, d) for x in (inp.q, inp.k, inp.v))
     do = inp.do_for(mode).reshape(B * H, N, d)
     for i in slices:
-        ref = a64.slice_reference(q[i], k[i], v[i], do[i], causal=True, scale=wl.scale)
+        ref = a64.slice_reference(q[i], k[i], v[i], do[i], causal=causal, scale=wl.scale)
         assert st.max_rel_err(g["o"].reshape(B * H, N, d)[i], ref["o"]) <= TOL[mode]
         lse_tol = 1e-4 if mode == "fp32_out" else 1e-2
         assert np.max(np.abs(g["lse"].reshape(B * H, N)[i] - ref["lse"])) <= lse_tol
@@ -416,8 +421,8 @@ def test_ragged_large_shapes(gpu, name, wl, slices, mode):
         band = np.zeros(N, bool)
         for r0 in range(0, N, 1024):
             pos = np.arange(r0, min(N, r0 + 1024))
-            fl, _, gap, top = fe.tie_flags_untiled(q[i][pos], k[i], q_pos=pos, scale=wl.scale,
-                                                   return_gap=True)
+            fl, _, gap, top = fe.tie_flags_untiled(q[i][pos], k[i], causal=causal, q_pos=pos,
+                                                   scale=wl.scale, return_gap=True)
             fl_ref[pos] = fl[0]
             band[pos] = np.abs(gap[0] - np.float32(1e-3)) <= 4 * f32_ulp(top[0])
         gf = g["flags"].reshape(B * H, N)[i]
