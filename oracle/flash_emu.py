@@ -97,8 +97,29 @@ class EmuResult:
     m_final: np.ndarray    # [S, R] the shift in force after the last tile
     obar: np.ndarray       # [S, R, d] FP32 accumulator before the epilogue
     l: np.ndarray          # [S, R] FP32 row sum of P-bar
-    n_pbar_one: np.ndarray  # [S, R] number of P-bar entries exactly equal to 1
+    n_pbar_one: np.ndarray  # [S, R] number of entries whose P-bar rounds to 1 in BF16
     max_pbar_flagged: np.ndarray  # [S, R] max P-bar over the tiles processed while the flag was set (-1 if none)
+    obar_one: np.ndarray   # [S, R, d] the part of obar from those entries (P-bar taken as 1)
+
+
+def pbar_one_threshold() -> float:
+    """The smallest FP32 value t for which P-bar = bf16(fp32(exp(t))) is 1.
+
+    P-bar is formed in FP32 and rounded to BF16 (nearest, ties to even).  BF16
+    below 1 has spacing 2^-8, so the FP32 value rounds to 1 exactly when it is
+    at least 1 - 2^-9 (the halfway point goes to the even 1.0); with a
+    correctly rounded FP32 exp that is exp(t) >= 1 - 2^-9 - 2^-25, just above
+    ln(1 - 2^-9) = -0.0019550...  The FP32 values t near it are 2^-32 apart;
+    float64 exp rounded to FP32 decides each of them.
+    """
+    target = np.float32(1.0 - 2.0 ** -9)
+    rn = lambda t: np.float32(np.exp(np.float64(t)))
+    t = np.float32(np.log(np.float64(target)))
+    while rn(t) < target:
+        t = np.nextafter(t, np.float32(0))
+    while rn(np.nextafter(t, np.float32(-1))) >= target:
+        t = np.nextafter(t, np.float32(-1))
+    return float(t)
 
 
 def _top2_multiset(s):
@@ -145,6 +166,8 @@ def flash_forward(q, k, v, mode="bf16_out", causal=True, scale=None, bn=64,
     el = np.zeros((ns, r))
     obar = np.zeros((ns, r, v.shape[2]))
     n_one = np.zeros((ns, r), np.int64)
+    obar_one = np.zeros_like(obar)
+    one_thr = pbar_one_threshold()
     flag = np.zeros((ns, r), bool)
     max_after = np.full((ns, r), -1.0)
 
@@ -181,8 +204,14 @@ def flash_forward(q, k, v, mode="bf16_out", causal=True, scale=None, bn=64,
         m_use = np.where(active, m_new, 0.0)
         # step 5-6: probabilities and the P-bar that enters the product
         with np.errstate(invalid="ignore"):
-            p = rd.exp(rd.r32(s - m_use[..., None]))
+            d_arg = rd.r32(s - m_use[..., None])
+            p = rd.exp(d_arg)
         p = np.where(np.isfinite(s), p, 0.0)
+        # the entries whose P-bar rounds to 1 in BF16 (the P-bar = 1 additions
+        # of section 3.4.4): decided on d = S - m against the threshold of a
+        # correctly rounded FP32 exp, the same entries in every mode
+        with np.errstate(invalid="ignore"):
+            ones = (np.isfinite(s) & (d_arg >= one_thr)).astype(F64)
         if hp and not rd.exact:
             hi = rd.bf(p)
             lo = rd.bf(rd.r32(p - hi))
@@ -191,13 +220,15 @@ def flash_forward(q, k, v, mode="bf16_out", causal=True, scale=None, bn=64,
             pbar = p
         else:
             pbar = rd.bf(p)
-        n_one += np.sum(pbar == 1.0, axis=-1)
+        n_one += np.sum(ones, axis=-1).astype(np.int64)
         tile_max = np.max(pbar, axis=-1)
         max_after = np.where(flag & active, np.maximum(max_after, tile_max), max_after)
         # step 7: FP32 accumulation, one rounding per tile
         el = np.where(active, rd.r32(alpha * el + np.sum(pbar, axis=-1)), el)
         obar_new = rd.r32(alpha[..., None] * obar + np.matmul(pbar, vt))
         obar = np.where(active[..., None], obar_new, obar)
+        one_new = rd.r32(alpha[..., None] * obar_one + np.matmul(ones, vt))
+        obar_one = np.where(active[..., None], one_new, obar_one)
         m = np.where(active, m_new, m)
 
     # step 8: epilogue
@@ -210,7 +241,7 @@ def flash_forward(q, k, v, mode="bf16_out", causal=True, scale=None, bn=64,
         lse = rd.r32(m + rd.log(el))
     return EmuResult(o=o, lse=lse, flag=flag, row_max=big_m, row_max2=big_m2,
                      m_final=m, obar=obar, l=el, n_pbar_one=n_one,
-                     max_pbar_flagged=max_after)
+                     max_pbar_flagged=max_after, obar_one=obar_one)
 
 
 def tie_flags_untiled(q, k, causal=True, scale=None, eps=1e-3, q_pos=None, return_gap=False):
@@ -244,3 +275,46 @@ def tie_flags_untiled(q, k, causal=True, scale=None, eps=1e-3, q_pos=None, retur
     with np.errstate(invalid="ignore"):
         gap = np.where(np.isfinite(top2), f32(top1 - top2).astype(F64), np.inf)
     return rs > 1, rs, gap, top1
+
+
+def tie_top2_untiled(q, k, causal=True, scale=None, eps=1e-3, q_pos=None, chunk=512):
+    """The untiled rule of tie_flags_untiled for one (batch, head) slice, stated
+    through the row's two largest scores: rs > 1 exactly when the second
+    largest score (multiset) lies within eps of the largest, because
+    fp32(rm - S) grows as S falls.  S is rounded as in flash_forward step 1.
+
+    q: [R, d] query rows, k: [N, d] keys (BF16 values); q_pos as in
+    tie_flags_untiled.  Rows are processed `chunk` at a time, so long
+    sequences need only chunk x N scores at once.  Returns (flag [R] bool,
+    gap [R] = fp32(M - M2), inf for a row with one visible key, M [R]).
+    """
+    q = np.asarray(q, F64)
+    k = np.asarray(k, F64)
+    r, d = q.shape
+    n = k.shape[0]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    q_pos = np.arange(r) if q_pos is None else np.asarray(q_pos)
+    s32 = F32(scale)
+    eps32 = F32(eps)
+    keys = np.arange(n)
+    flag = np.zeros(r, bool)
+    gap = np.empty(r, F32)
+    top = np.empty(r, F32)
+    kt = np.ascontiguousarray(k.T)
+    for r0 in range(0, r, chunk):
+        r1 = min(r, r0 + chunk)
+        s = (q[r0:r1] @ kt).astype(F32) * s32        # fp32(fp32(q.k) * fp32(scale))
+        if causal:
+            s[keys[None, :] > q_pos[r0:r1, None]] = -np.inf
+        m1 = s.max(axis=1)
+        at_max = s == m1[:, None]
+        n_max = at_max.sum(axis=1)
+        s[at_max] = -np.inf
+        m2 = np.where(n_max >= 2, m1, s.max(axis=1))
+        with np.errstate(invalid="ignore"):
+            g = np.where(np.isfinite(m2), m1 - m2, F32(np.inf)).astype(F32)
+        gap[r0:r1] = g
+        top[r0:r1] = m1
+        flag[r0:r1] = np.isfinite(m2) & (g <= eps32)
+    return flag, gap, top

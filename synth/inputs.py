@@ -109,7 +109,7 @@ def _force_ties(rng, q, k, rows, tie_q_scale):
         sc = k[: t_row + 1].astype(np.float64) @ q[t_row].astype(np.float64)
         t_star = int(np.argmax(sc))
         kk = int(rng.integers(2, 5))
-        others = np.setdiff1d(np.arange(t_row + 1), [t_star])
+        others = np.delete(np.arange(t_row + 1), t_star)   # [0, T] without t*, in order
         pos = rng.choice(others, size=kk - 1, replace=False)
         k[pos] = k[t_star]
         done.append((t_row, kk))

@@ -8,7 +8,7 @@ import pytest
 from oracle import attention64 as a64
 from oracle import flash_emu as fe
 from oracle import stats as st
-from oracle.numerics import is_bf16
+from oracle.numerics import bf16_rne, f32, is_bf16
 from synth.inputs import generate, generate_reps, to_bf16_values, workload
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
@@ -231,3 +231,103 @@ def test_flag_one_ulp_either_side_of_eps():
                                  causal=True, scale=0.125, bn=bn)
             assert bool(r.flag[0][T]) == expect[h]
             assert np.array_equal(r.flag[0], fl[0])
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_top2_statement_equals_the_rs_rule(causal):
+    """tie_top2_untiled (the rule through the two largest scores) against the
+    pages' count form rs = rowsum(rm - S <= eps) > 1: forced ties (config 1),
+    natural ties of sharp rows (config 3's Q x4), the one-ulp eps boundary
+    inputs and eps = 0."""
+    from eps_boundary import boundary_inputs
+    cases = []
+    x = generate(workload(1))
+    cases.append((x.q[0, 0], x.k[0, 0], 0.125, 1e-3))
+    x3 = generate(workload(3, b=1, h=2, n=300))
+    cases += [(x3.q[0, h], x3.k[0, h], 0.125, 1e-3) for h in range(2)]
+    cases.append((x3.q[0, 0], x3.k[0, 0], 0.125, 0.0))
+    qb, kb, _, _ = boundary_inputs()
+    cases += [(qb[0, h], kb[0, h], 0.125, 1e-3) for h in range(qb.shape[1])]
+    for q, k, scale, eps in cases:
+        fl, rs, gap, top = fe.tie_flags_untiled(q, k, causal=causal, scale=scale, eps=eps, return_gap=True)
+        f2, g2, t2 = fe.tie_top2_untiled(q, k, causal=causal, scale=scale, eps=eps, chunk=37)
+        assert np.array_equal(f2, fl[0])
+        assert np.array_equal(t2.astype(np.float64), top[0])
+        fin = np.isfinite(gap[0])
+        assert np.array_equal(np.isfinite(g2), fin)
+        assert np.array_equal(g2[fin].astype(np.float64), gap[0][fin])
+    assert sum(int(fe.tie_top2_untiled(q, k, causal=causal, scale=s, eps=e)[0].sum())
+               for q, k, s, e in cases) > 10
+
+
+def test_pbar_one_threshold_is_the_bf16_rounding_boundary():
+    """At the threshold t, exp rounded to FP32 is 1 - 2^-9, which BF16 rounds
+    (ties to even) to 1; one FP32 step lower it is 1 - 2^-9 - 2^-24, which
+    rounds to 1 - 2^-8.  t is the first FP32 value (spacing 2^-32 there) at or
+    above ln(1 - 2^-9 - 2^-25) = -0.00195506...
+    (numpy's own FP32 exp is not correctly rounded there: it gives 1 - 2^-9
+    one step below t, which is why the count uses this threshold.)"""
+    from oracle.numerics import bf16_rne
+    t = np.float32(fe.pbar_one_threshold())
+    below = np.nextafter(t, np.float32(-1))
+    for x, fp32, b16 in ((t, 1 - 2.0 ** -9, 1.0), (below, 1 - 2.0 ** -9 - 2.0 ** -24, 1 - 2.0 ** -8)):
+        e = np.float32(np.exp(np.float64(x)))
+        assert e == np.float32(fp32)
+        assert bf16_rne(e) == np.float32(b16)
+    assert 0 <= float(t) - np.log1p(-2.0 ** -9 - 2.0 ** -25) < 2.0 ** -32
+
+
+@pytest.mark.parametrize("bn", [32, 64])
+def test_pbar_one_count_matches_the_rounded_pbar(bn):
+    """The count equals the number of entries of the rounded P-bar that are
+    exactly 1 in the plain mode (no entry of these inputs sits within the FP32
+    exp error of the threshold), and the FP32-output mode counts the same
+    entries (same running maximum)."""
+    x = generate_reps(workload(1), 4)
+    b = x.q.shape[0]
+    q, k, v = (a.reshape(b, 128, 64) for a in (x.q, x.k, x.v))
+    r = fe.flash_forward(q, k, v, mode="bf16_out", bn=bn)
+    rh = fe.flash_forward(q, k, v, mode="fp32_out", bn=bn)
+    assert np.array_equal(r.n_pbar_one, rh.n_pbar_one)
+    # recount: the rounded P-bar of each tile, with the row maximum known
+    # after the tile as the shift
+    cnt = np.zeros((b, 128), np.int64)
+    big = np.full((b, 128), -np.inf)
+    for j0 in range(0, 128, bn):
+        x_ = f32(np.matmul(q.astype(np.float64), k[:, j0:j0 + bn].transpose(0, 2, 1).astype(np.float64)))
+        s_ = f32(x_.astype(np.float64) * np.float64(np.float32(0.125))).astype(np.float64)
+        s_ = np.where(np.arange(j0, j0 + bn)[None, None, :] > np.arange(128)[None, :, None], -np.inf, s_)
+        big = np.maximum(big, s_.max(axis=-1))
+        with np.errstate(invalid="ignore"):
+            pb = bf16_rne(np.exp(f32(s_ - big[..., None])))
+        cnt += np.sum(pb == 1.0, axis=-1)
+    assert np.array_equal(cnt, r.n_pbar_one)
+    fl, rs = fe.tie_flags_untiled(q, k, eps=0.0)
+    assert np.all(r.n_pbar_one >= rs) and np.all(r.n_pbar_one[fl] >= 2)
+    assert r.n_pbar_one.sum() > b * 128
+
+
+def test_pbar_one_part_of_obar_on_the_hand_tie():
+    """The hand-built tie (tests/golden/hand_tie_example.json): in the plain
+    mode the P-bar = 1 entries of rows 1 and 2 are keys 0 and 1, whose V sum
+    -2.296875 - 2.40625 = -4.703125 is exact in FP32, and row 0's is key 0; in
+    the tie-aware mode the shift 2 * 8 leaves no entry at 1 on the tied rows."""
+    d = 64
+    q = np.zeros((3, d), np.float32)
+    q[:, 0] = 64.0
+    k = np.zeros((3, d), np.float32)
+    k[0, 0] = k[1, 0] = 1.0
+    k[2, 0] = 0.25
+    v = np.zeros((3, d), np.float32)
+    v[:, 0] = (-2.296875, -2.40625, -2.0)
+    v[:, 1] = -v[:, 0]
+    r = fe.flash_forward(q, k, v, mode="bf16_out", scale=1 / 8)
+    assert list(r.n_pbar_one[0]) == [1, 2, 2]
+    assert list(r.obar_one[0, :, 0]) == [-2.296875, -4.703125, -4.703125]
+    assert list(r.obar_one[0, :, 1]) == [2.296875, 4.703125, 4.703125]
+    assert np.all(r.obar_one[0, :, 2:] == 0.0)
+    t = fe.flash_forward(q, k, v, mode="tie_aware_softmax", scale=1 / 8)
+    assert list(t.n_pbar_one[0]) == [1, 0, 0]
+    assert list(t.obar_one[0, :, 0]) == [-2.296875, 0.0, 0.0]
+    h = fe.flash_forward(q, k, v, mode="fp32_out", scale=1 / 8)
+    assert np.array_equal(h.n_pbar_one, r.n_pbar_one) and np.array_equal(h.obar_one, r.obar_one)
