@@ -101,17 +101,31 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int mode, const pfa_tie_opts* opts, void* stream);
 
 /*
- * attn_fwd plus a diagnostic: pbar_one (out, INT32 [B,H,N], device, required)
- * counts per row the P-bar entries that round to 1 in BF16, i.e. exp(S - m) >=
- * 1 - 2^-9.  In the BF16 modes these are exactly the P-bar = 1 additions at
- * which the pages' cumulative error of O-bar jumps (section 3.4.4, "Why P-bar =
- * 1 is the critical condition"); in PFA_FP32_OUT the same entries (there they
- * enter as hi + lo, within 2^-9 of 1).  Same outputs as attn_fwd otherwise;
- * runs a separate kernel variant, so attn_fwd pays nothing for it.
+ * attn_fwd plus two diagnostics of the P-bar = 1 additions at which the pages'
+ * cumulative error of O-bar jumps (section 3.4.4, "How the error accumulates
+ * across token positions" and "Why P-bar = 1 is the critical condition"):
+ *
+ *   pbar_one  out  INT32 [B,H,N], device, required: per row, the number of
+ *                  entries whose P-bar rounds to 1 in BF16.  Decided on the
+ *                  method's definition: S = fp32(fp32(q.k) * scale),
+ *                  d = fp32(S - m) with m the shift in force for the entry's
+ *                  key tile, and P-bar = bf16(fp32(exp(d))) is 1 exactly
+ *                  when exp(d), correctly rounded to FP32, is at least
+ *                  1 - 2^-9.  The same entries in every mode (in
+ *                  PFA_FP32_OUT they enter the product as hi + lo, within
+ *                  2^-9 of 1).
+ *   o_one     out  FP32 [B,H,N,d], device, 16-byte aligned, or NULL: the part
+ *                  of O those entries carry, (sum of their V rows, rescaled
+ *                  with O-bar from tile to tile) / rowsum(P-bar), kept apart
+ *                  from the rest of O.
+ *
+ * Same outputs as attn_fwd otherwise; runs a separate kernel variant, so
+ * attn_fwd pays nothing for it.  Errors as attn_fwd, plus PFA_ERR_INVALID for
+ * a NULL or misaligned pbar_one or a misaligned o_one.
  */
 int attn_fwd_diag(const void* q, const void* k, const void* v, void* o, float* lse,
-                  int32_t* tie_flags, int32_t* pbar_one, int B, int H, int N, int d, int causal,
-                  float scale, int mode, const pfa_tie_opts* opts, void* stream);
+                  int32_t* tie_flags, int32_t* pbar_one, float* o_one, int B, int H, int N, int d,
+                  int causal, float scale, int mode, const pfa_tie_opts* opts, void* stream);
 
 /*
  * Forward with a mode per head: the pages' localisation experiment computes O

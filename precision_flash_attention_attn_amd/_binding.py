@@ -67,7 +67,7 @@ def lib() -> ctypes.CDLL:
         L.attn_bwd_ex.restype = i
         L.attn_delta_error.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
         L.attn_delta_error.restype = i
-        L.attn_fwd_diag.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i,
+        L.attn_fwd_diag.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i,
                                     ctypes.POINTER(TieOpts), vp]
         L.attn_fwd_diag.restype = i
         L.attn_fwd_heads.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp,
@@ -136,9 +136,10 @@ def attn_fwd(q, k, v, o, lse, tie_flags=None, causal=True, scale=None, mode="bf1
                           _stream(stream)))
 
 
-def attn_fwd_diag(q, k, v, o, lse, tie_flags, pbar_one, causal=True, scale=None, mode="bf16_out",
-                  beta=2.0, eps=1e-3, stream=None):
-    """attn_fwd plus the per-row count of P-bar entries equal to 1 (pbar_one, int32)."""
+def attn_fwd_diag(q, k, v, o, lse, tie_flags, pbar_one, o_one=None, causal=True, scale=None,
+                  mode="bf16_out", beta=2.0, eps=1e-3, stream=None):
+    """attn_fwd plus the per-row count of P-bar entries that round to 1
+    (pbar_one, int32) and, if given, the part of O they carry (o_one, FP32)."""
     B, H, N, d = q.shape
     mid = _mode_id(mode)
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -148,10 +149,12 @@ def attn_fwd_diag(q, k, v, o, lse, tie_flags, pbar_one, causal=True, scale=None,
     if tie_flags is not None:
         _expect(tie_flags, "tie_flags", torch.int32, (B, H, N))
     _expect(pbar_one, "pbar_one", torch.int32, (B, H, N))
+    if o_one is not None:
+        _expect(o_one, "o_one", torch.float32, (B, H, N, d))
     scale = 1.0 / d ** 0.5 if scale is None else float(scale)
     opts = TieOpts(float(beta), float(eps))
     _check(lib().attn_fwd_diag(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(tie_flags),
-                               _ptr(pbar_one), B, H, N, d, int(bool(causal)), scale, mid,
+                               _ptr(pbar_one), _ptr(o_one), B, H, N, d, int(bool(causal)), scale, mid,
                                ctypes.byref(opts), _stream(stream)))
 
 

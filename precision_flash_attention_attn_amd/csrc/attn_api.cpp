@@ -27,6 +27,20 @@ int check_sizes(int B, int H, int N, int d) {
   return PFA_OK;
 }
 
+// The smallest FP32 value t for which P-bar = bf16(fp32(exp(t))) is 1 (BF16
+// round to nearest even): the FP32 value must be at least 1 - 2^-9, the
+// halfway point below 1 that goes to the even 1.0.  exp is taken correctly
+// rounded to FP32 (double exp, then rounded): the candidates near t are 2^-32
+// apart, and none of their exponentials lies near an FP32 halfway point.
+float pbar_one_threshold() {
+  const float target = 1.0f - 1.0f / 512.0f;
+  const auto rn = [](float t) { return static_cast<float>(std::exp(static_cast<double>(t))); };
+  float t = static_cast<float>(std::log(static_cast<double>(target)));
+  while (rn(t) < target) t = std::nextafter(t, 0.0f);
+  while (rn(std::nextafter(t, -1.0f)) >= target) t = std::nextafter(t, -1.0f);
+  return t;
+}
+
 int check_common(int B, int H, int N, int d, float scale, int mode) {
   const int s = check_sizes(B, H, N, d);
   if (s != PFA_OK) return s;
@@ -43,8 +57,8 @@ extern "C" {
 namespace {
 
 int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int32_t* tie_flags,
-             int32_t* pbar_one, int B, int H, int N, int d, int causal, float scale, int mode,
-             const pfa_tie_opts* opts, void* stream) {
+             int32_t* pbar_one, float* o_one, int B, int H, int N, int d, int causal, float scale,
+             int mode, const pfa_tie_opts* opts, void* stream) {
   int st = check_common(B, H, N, d, scale, mode);
   if (st != PFA_OK) return st;
   if (!q || !k || !v || !o || !lse) return PFA_ERR_INVALID;
@@ -76,6 +90,11 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
   a.beta = beta;
   a.eps = eps;
   a.pbar_one = pbar_one;
+  a.o_one = o_one;
+  if (pbar_one) {
+    static const float thr = pbar_one_threshold();
+    a.one_thr = thr;
+  }
   const hipError_t e = pfa::launch_fwd(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PFA_OK : PFA_ERR_HIP;
 }
@@ -85,14 +104,17 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int32_t* tie_flags,
              int B, int H, int N, int d, int causal, float scale, int mode,
              const pfa_tie_opts* opts, void* stream) {
-  return fwd_impl(q, k, v, o, lse, tie_flags, nullptr, B, H, N, d, causal, scale, mode, opts, stream);
+  return fwd_impl(q, k, v, o, lse, tie_flags, nullptr, nullptr, B, H, N, d, causal, scale, mode, opts,
+                  stream);
 }
 
 int attn_fwd_diag(const void* q, const void* k, const void* v, void* o, float* lse,
-                  int32_t* tie_flags, int32_t* pbar_one, int B, int H, int N, int d, int causal,
-                  float scale, int mode, const pfa_tie_opts* opts, void* stream) {
+                  int32_t* tie_flags, int32_t* pbar_one, float* o_one, int B, int H, int N, int d,
+                  int causal, float scale, int mode, const pfa_tie_opts* opts, void* stream) {
   if (!pbar_one || !aligned4(pbar_one)) return PFA_ERR_INVALID;
-  return fwd_impl(q, k, v, o, lse, tie_flags, pbar_one, B, H, N, d, causal, scale, mode, opts, stream);
+  if (o_one && !aligned16(o_one)) return PFA_ERR_INVALID;
+  return fwd_impl(q, k, v, o, lse, tie_flags, pbar_one, o_one, B, H, N, d, causal, scale, mode, opts,
+                  stream);
 }
 
 int attn_fwd_heads(const void* q, const void* k, const void* v, float* o, float* lse,

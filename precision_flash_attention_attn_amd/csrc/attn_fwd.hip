@@ -57,6 +57,8 @@ struct FwdParams {
   int H, filter, o_f32;
   uint64_t hmask[4];
   int32_t* pbar_one;     // diagnostic variant: per-row count of P-bar entries equal to 1
+  float* o_one;          // diagnostic variant: the part of O from those entries (NULL: skip)
+  float one_thr;         // the smallest FP32 d with bf16(fp32(exp(d))) = 1 (P-bar rounds to 1)
 };
 
 // Row order of K inside a 32-key block: MFMA accumulator row i of lane half h
@@ -82,12 +84,16 @@ __device__ __forceinline__ void map_block(int bid, int BH, int nqb, int& bh, int
 }
 
 // DIAG (a diagnostic variant, always with FLAGS): also count, per row, the
-// P-bar entries that round to 1 in BF16 -- in the BF16 modes exactly the
-// P-bar = 1 additions the pages' cumulative-error trace singles out (section
-// 3.4.4, "Why P-bar = 1 is the critical condition").  In the FP32-output mode
-// the entries carry 1 - e (the exponent comes from one fma of the raw dot
-// product, whose rounding residue survives the hi + lo split) and the count is
-// of their BF16 hi part.
+// P-bar entries that round to 1 in BF16 -- the P-bar = 1 additions the pages'
+// cumulative-error trace singles out (section 3.4.4, "Why P-bar = 1 is the
+// critical condition") -- and accumulate the part of O-bar they carry (their
+// V rows, rescaled with O-bar), kept apart from the rest.  The decision
+// follows the method's definition of P-bar rather than the fast exponent of
+// the product: S = fp32(dot * scale), d = fp32(S - m), and P-bar rounds to 1
+// exactly when fp32(exp(d)) >= 1 - 2^-9 (exp correctly rounded), i.e.
+// d >= one_thr.  The same entries are
+// counted in every mode (in the FP32-output mode they enter the product as
+// hi + lo within 2^-9 of 1).
 template <int D, int MODE, bool CAUSAL, bool FLAGS, bool DIAG, bool WIDE>
 struct FwdKernel {
   // WIDE (d = 128 with fewer than 32 (batch, head) slices): 8 waves over 256
@@ -99,7 +105,9 @@ struct FwdKernel {
   // Two waves per SIMD either way.
   static_assert(!WIDE || D == 128, "the 256-query geometry is built for d = 128");
   static constexpr int BM = WIDE ? 256 : 128, BN = 64, NT = BM * 2;
-  static constexpr int MIN_WG = WIDE ? 1 : 2;
+  // The diagnostic variant keeps a second O-bar accumulator: one workgroup
+  // per CU, so each wave may hold up to 512 registers.
+  static constexpr int MIN_WG = (WIDE || DIAG) ? 1 : 2;
   static constexpr int CH = D / 8;    // 16-byte chunks per K/V row
   static constexpr int DC = D / 16;   // contraction steps of K Q^T
   static constexpr int KB = BN / 32;  // 32-key blocks per tile
@@ -134,6 +142,7 @@ struct FwdKernel {
   float Mraw, M2raw, m, mb, alpha, lsum;
   bool flag;
   int n_one;             // DIAG: this lane's count of P-bar == 1
+  f32x16 oone[DIAG ? DB : 1];  // DIAG: O-bar^T of the P-bar == 1 entries alone
 
   __device__ FwdKernel(const FwdParams& p_, char* k0, char* k1, char* v0, char* v1)
       : p(p_), kb0(k0), kb1(k1), vb0(v0), vb1(v1) {}
@@ -233,12 +242,27 @@ struct FwdKernel {
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      if (DIAG)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oone[db][r] *= alpha;
     }
+  }
+
+  // DIAG: 1 when the score with raw dot product x gives a P-bar that rounds to
+  // 1 in BF16 under the current shift m (see the DIAG note above).
+  __device__ __forceinline__ uint32_t is_one(float x) {
+#pragma clang fp contract(off)
+    const float sv = x * p.scale;
+    const float dv = sv - m;
+    return dv >= p.one_thr ? 1u : 0u;
   }
 
   // P-bar = exp(S - m) rounded to BF16 (plus the BF16 remainder in the FP32
   // output mode), and l = l alpha + its row sum.
-  __device__ __forceinline__ void softmax(const f32x16 (&s)[KB], uint32_t (&pk)[KB][8], uint32_t (&pl)[KB][8]) {
+  __device__ __forceinline__ void softmax(const f32x16 (&s)[KB], uint32_t (&pk)[KB][8], uint32_t (&pl)[KB][8],
+                                          uint32_t (&po)[KB][8]) {
     const float c1 = p.scale * kLog2e;
     float lt = 0.f;
 #pragma unroll
@@ -257,9 +281,10 @@ struct FwdKernel {
           lt = add_bf16_pair(ul, lt);
         }
         if (DIAG) {
-          // P-bar rounds to BF16 1.0 (0x3f80); in the FP32-output mode this is the hi part
-          n_one += ((u & 0xffffu) == 0x3f80u) ? 1 : 0;
-          n_one += ((u >> 16) == 0x3f80u) ? 1 : 0;
+          // the entries whose P-bar rounds to 1, as a BF16 pair of 1.0 / 0 values
+          const uint32_t ia = is_one(s[kb][2 * i]), ib = is_one(s[kb][2 * i + 1]);
+          n_one += (int)(ia + ib);
+          po[kb][i] = (ia ? 0x3f80u : 0u) | (ib ? 0x3f800000u : 0u);
         }
       }
     lsum = fmaf(lsum, alpha, lt);
@@ -267,7 +292,8 @@ struct FwdKernel {
 
   // O^T += V^T P-bar^T from V buffer B.
   template <int B>
-  __device__ __forceinline__ void pv(const uint32_t (&pk)[KB][8], const uint32_t (&pl)[KB][8]) {
+  __device__ __forceinline__ void pv(const uint32_t (&pk)[KB][8], const uint32_t (&pl)[KB][8],
+                                     const uint32_t (&po)[KB][8]) {
     const char* vl = B ? vb1 : vb0;
     int v0s = vbase0, v1s = vbase1;
     asm volatile("" : "+v"(v0s), "+v"(v1s));
@@ -285,6 +311,10 @@ struct FwdKernel {
           const u32x4 bl = u32x4{pl[kb][o4], pl[kb][o4 + 1], pl[kb][o4 + 2], pl[kb][o4 + 3]};
           oacc[db] = mfma_bf16(aop, bl, oacc[db]);
         }
+        if (DIAG) {
+          const u32x4 bo = u32x4{po[kb][o4], po[kb][o4 + 1], po[kb][o4 + 2], po[kb][o4 + 3]};
+          oone[db] = mfma_bf16(aop, bo, oone[db]);
+        }
       }
     }
   }
@@ -301,9 +331,9 @@ struct FwdKernel {
     rescale();
     f32x16 sn[KB];
     qk<1 - P>(sn);
-    uint32_t pk[KB][8], pl[KB][8];
-    softmax(scur, pk, pl);
-    pv<P>(pk, pl);
+    uint32_t pk[KB][8], pl[KB][8], po[KB][8];
+    softmax(scur, pk, pl, po);
+    pv<P>(pk, pl, po);
     if (MASKN) mask(sn, (j + 1) * BN);
     update_max(sn);
 #pragma unroll
@@ -315,9 +345,9 @@ struct FwdKernel {
   template <int P>
   __device__ __forceinline__ void last() {
     rescale();
-    uint32_t pk[KB][8], pl[KB][8];
-    softmax(scur, pk, pl);
-    pv<P>(pk, pl);
+    uint32_t pk[KB][8], pl[KB][8], po[KB][8];
+    softmax(scur, pk, pl, po);
+    pv<P>(pk, pl, po);
   }
 
   __device__ __forceinline__ void run() {
@@ -358,6 +388,9 @@ struct FwdKernel {
     vbase1 = swz_elem<CH>(tr_row + 4, tr_col);
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+    if (DIAG)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oone[db] = f32x16{};
     Mraw = kNegInf;
     M2raw = kNegInf;
     m = kNegInf;
@@ -380,6 +413,10 @@ struct FwdKernel {
     qk<0>(scur);
     mask(scur, 0);
     update_max(scur);
+    // Step 0 loads K(2) into the buffer that holds K(0): every wave must have
+    // read K(0) first.  (Later steps are covered by the barrier that ends the
+    // step before.)
+    if (n_tiles > 2) __syncthreads();
 
     // steps 0 .. n_tiles-2, in pairs so that buffer indices are compile-time
     // constants; a step masks the scores of its next tile unless that tile is
@@ -417,6 +454,17 @@ struct FwdKernel {
     }
     if (myq >= N) return;
     const size_t orow = base + (size_t)myq * D;
+    if (DIAG && p.o_one) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int d0 = 32 * db + 8 * rr + 4 * hi;
+          const f32x4 out = {oone[db][4 * rr] / ltot, oone[db][4 * rr + 1] / ltot,
+                             oone[db][4 * rr + 2] / ltot, oone[db][4 * rr + 3] / ltot};
+          *reinterpret_cast<f32x4*>(p.o_one + orow + d0) = out;
+        }
+    }
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -491,8 +539,11 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   p.o_f32 = a.o_f32;
   for (int i = 0; i < 4; ++i) p.hmask[i] = a.hmask[i];
   p.pbar_one = a.pbar_one;
-  // the 256-query geometry for fewer than 32 slices at d = 128 (see FwdKernel)
-  if constexpr (D == 128)
+  p.o_one = a.o_one;
+  p.one_thr = a.one_thr;
+  // the 256-query geometry for fewer than 32 slices at d = 128 (see FwdKernel);
+  // the diagnostic variant always runs 128-query workgroups
+  if constexpr (D == 128 && !DIAG)
     if (p.BH < 32) return launch_g<D, MODE, CAUSAL, FLAGS, DIAG, true>(p, stream);
   return launch_g<D, MODE, CAUSAL, FLAGS, DIAG, false>(p, stream);
 }

@@ -28,6 +28,8 @@ struct FwdArgs {
   int filter = 0, o_f32 = 0;
   uint64_t hmask[4] = {0, 0, 0, 0};
   int32_t* pbar_one = nullptr;   // attn_fwd_diag: per-row count of P-bar == 1
+  float* o_one = nullptr;        // attn_fwd_diag: the part of O from those entries (optional)
+  float one_thr = 0.f;           // smallest FP32 d with exp(d) >= 1 - 2^-9
 };
 
 struct BwdArgs {

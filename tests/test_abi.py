@@ -187,7 +187,9 @@ def test_per_head_forward_rejects_invalid_arguments(L):
 
 def test_diag_forward_requires_the_count_buffer(L):
     inv = bnd.PFA_ERR_INVALID
-    f = lambda cnt: L.attn_fwd_diag(FAKE, FAKE, FAKE, FAKE, FAKE, None, cnt, 1, 1, 128, 64, 1, 0.125, 0,
-                                    None, None)
+    f = lambda cnt, one=None: L.attn_fwd_diag(FAKE, FAKE, FAKE, FAKE, FAKE, None, cnt, one, 1, 1, 128, 64, 1,
+                                              0.125, 0, None, None)
     assert f(None) == inv
     assert f(FAKE + 2) == inv
+    assert f(FAKE, one=FAKE + 4) == inv   # o_one must be 16-byte aligned
+

@@ -1,16 +1,13 @@
 """GPU parity of the diagnostic forward (attn_fwd_diag): its O, LSE and tie
-flags are the plain forward's bit for bit, and its per-row count of P-bar
-entries that round to 1 in BF16 (the P-bar = 1 additions the pages'
-cumulative-error trace singles out, paper-graph-ui summary of arXiv 2510.04212,
-section 3.4.4) agrees with the BF16 flash emulator's count (for the FP32-output
-mode: the BF16 mode's count, which has the same running maximum).
+flags are the plain forward's bit for bit; its per-row count of P-bar entries
+that round to 1 in BF16 (the P-bar = 1 additions the pages' cumulative-error
+trace singles out, paper-graph-ui summary of arXiv 2510.04212, section 3.4.4)
+equals the BF16 flash emulator's count on every row; and the part of O those
+entries carry (o_one) agrees with the emulator's to FP32 accuracy.
 
-The count is an integer decided by floating point: P-bar rounds to 1 when
-exp(S - m) >= 1 - 2^-9.  The kernel forms the exponent with one fma from the
-raw dot product, the emulator rounds S and S - m separately, so an element
-whose exponent lies within an ulp of that boundary can fall on either side.
-Such elements are rare; the bar is equal counts on at least 98% of rows and
-totals within 1%.
+The count is an integer decided by floating point: both sides decide it on
+d = fp32(fp32(q.k) * scale) - m against the threshold of a correctly rounded
+FP32 exp (P-bar = bf16(fp32(exp(d))) is 1), so the counts must be equal.
 """
 from __future__ import annotations
 
@@ -29,8 +26,10 @@ CASES = [
     ("ragged333_d64", Workload(90, "ragged", 1, 2, 333, 64, tie_frac=0.05, tie_q_scale=4.0), True),
     ("b2_n200_d128", Workload(91, "d128", 2, 1, 200, 128, tie_frac=0.05, tie_q_scale=4.0), True),
     ("noncausal_n257_d128", Workload(94, "nc", 1, 3, 257, 128, tie_frac=0.05, tie_q_scale=8.0), False),
-    # 32 (batch, head) slices at d = 128: the forward's 128-query geometry
+    # 32 (batch, head) slices at d = 128
     ("bh32_n160_d128", Workload(95, "bh32", 2, 16, 160, 128, tie_frac=0.05, tie_q_scale=4.0), True),
+    # several key tiles with sharp rows whose maximum moves (the rescale of o_one)
+    ("n1000_d128_q4", Workload(96, "sharp", 1, 2, 1000, 128, q_scale=4.0, tie_frac=0.02, tie_q_scale=2.0), True),
 ]
 
 
@@ -42,50 +41,57 @@ def gpu():
     return gpu_util
 
 
-@pytest.mark.parametrize("mode", ["bf16_out", "fp32_out", "tie_aware_softmax"])
-@pytest.mark.parametrize("name,wl,causal", CASES, ids=[c[0] for c in CASES])
-def test_pbar_one_count(gpu, name, wl, causal, mode):
+def _diag(gpu, wl, causal, mode):
     import precision_flash_attention_attn_amd as pfa
-    print(f"[diag] {name} mode={mode}", flush=True)
     inp = generate(wl)
     q, k, v = gpu.dev_bf16(inp.q), gpu.dev_bf16(inp.k), gpu.dev_bf16(inp.v)
     o, lse, fl = pfa.forward(q, k, v, causal=causal, mode=mode)
     o2, lse2, fl2 = torch.empty_like(o), torch.empty_like(lse), torch.empty_like(fl)
     cnt = torch.empty_like(fl)
-    pfa.attn_fwd_diag(q, k, v, o2, lse2, fl2, cnt, causal=causal, mode=mode)
+    one = torch.full(q.shape, 7.0, device=q.device, dtype=torch.float32)
+    pfa.attn_fwd_diag(q, k, v, o2, lse2, fl2, cnt, one, causal=causal, mode=mode)
     torch.cuda.synchronize()
     assert torch.equal(o, o2) and torch.equal(lse, lse2) and torch.equal(fl, fl2)
+    return inp, gpu.host(lse2), cnt.cpu().numpy(), gpu.host(one)
+
+
+@pytest.mark.parametrize("mode", ["bf16_out", "fp32_out", "tie_aware_softmax"])
+@pytest.mark.parametrize("name,wl,causal", CASES, ids=[c[0] for c in CASES])
+def test_pbar_one_count_and_part_of_o(gpu, name, wl, causal, mode):
+    print(f"[diag] {name} mode={mode}", flush=True)
+    inp, lse, cnt, one = _diag(gpu, wl, causal, mode)
     B, H, N, d = wl.b, wl.h, wl.n, wl.d
-    # the count is of P-bar rounded to BF16; in the FP32-output mode the running
-    # maximum, and so exp(S - m), is that of the plain BF16 mode
-    emu_mode = "bf16_out" if mode == "fp32_out" else mode
-    emu = fe.flash_forward(*(x.reshape(B * H, N, d) for x in (inp.q, inp.k, inp.v)), mode=emu_mode,
+    emu = fe.flash_forward(*(x.reshape(B * H, N, d) for x in (inp.q, inp.k, inp.v)), mode=mode,
                            causal=causal, scale=wl.scale)
-    got = cnt.cpu().numpy().reshape(B * H, N)
-    want = emu.n_pbar_one
-    agree = np.mean(got == want)
-    print(f"  rows with equal counts: {agree:.4f}; totals {got.sum()} vs {want.sum()}")
-    assert agree >= 0.98
-    assert abs(int(got.sum()) - int(want.sum())) <= 0.01 * want.sum() + 2
+    got = cnt.reshape(B * H, N)
+    print(f"  P-bar = 1 entries: gpu {int(got.sum())} oracle {int(emu.n_pbar_one.sum())}; rows that "
+          f"differ {int(np.sum(got != emu.n_pbar_one))}", flush=True)
+    assert np.array_equal(got, emu.n_pbar_one)
+    if mode != "tie_aware_softmax":
+        assert np.all(got >= 1)          # every row has its maximum at least
+    # o_one * l with l from the kernel's own LSE (l = exp(LSE - m), m the
+    # emulator's final shift, the same FP32 value as the kernel's) against the
+    # emulator's FP32 sum: the same V rows, summed in another order.  The
+    # bound is FP32 level: LSE (|LSE| < 128 here) is rounded to 2^-17, which
+    # carries into l as 7.6e-6 relative, plus the two sums' roundings.
+    ell = np.exp(lse.reshape(B * H, N) - emu.m_final)
+    got_bar = one.reshape(B * H, N, d) * ell[..., None]
+    want = emu.obar_one
+    scale_ = np.max(np.abs(want), axis=-1, keepdims=True) + 1e-30
+    rel = np.max(np.abs(got_bar - want) / scale_)
+    print(f"  o_one: max error {rel:.2e} of the row's largest entry", flush=True)
+    assert rel <= 4e-5
+    # rows without P-bar = 1 entries carry no such part
+    assert np.all(one.reshape(B * H, N, d)[emu.n_pbar_one == 0] == 0.0)
 
 
 def test_pbar_one_count_natural_ties(gpu):
     """GPT-2-medium shape with natural ties only (B8 H16 N1024 d64, Q x4):
-    the counts of batch 0 against the emulator, head by head."""
-    import precision_flash_attention_attn_amd as pfa
+    the counts of batch 0 against the emulator, head by head, on every row."""
     wl = workload(3)
-    inp = generate(wl)
-    q, k, v = gpu.dev_bf16(inp.q), gpu.dev_bf16(inp.k), gpu.dev_bf16(inp.v)
-    B, H, N, d = q.shape
-    o = torch.empty_like(q)
-    lse = torch.empty((B, H, N), device=q.device, dtype=torch.float32)
-    fl = torch.empty((B, H, N), device=q.device, dtype=torch.int32)
-    cnt = torch.empty_like(fl)
-    pfa.attn_fwd_diag(q, k, v, o, lse, fl, cnt)
-    torch.cuda.synchronize()
-    got = cnt[0].cpu().numpy()
+    inp, lse, cnt, one = _diag(gpu, wl, True, "bf16_out")
+    got = cnt[0]
     emu = fe.flash_forward(inp.q[0], inp.k[0], inp.v[0], mode="bf16_out", causal=True, scale=wl.scale)
-    agree = np.mean(got == emu.n_pbar_one)
-    print(f"  rows with equal counts: {agree:.4f}; totals {got.sum()} vs {emu.n_pbar_one.sum()}")
-    assert agree >= 0.98
-    assert abs(int(got.sum()) - int(emu.n_pbar_one.sum())) <= 0.01 * emu.n_pbar_one.sum() + 2
+    print(f"  rows that differ {int(np.sum(got != emu.n_pbar_one))}; totals {got.sum()} vs "
+          f"{emu.n_pbar_one.sum()}", flush=True)
+    assert np.array_equal(got, emu.n_pbar_one)
