@@ -3,10 +3,16 @@
 Tolerances: max relative error (normwise, max|x - ref| / max|ref|) against
 the float64 attention of at most 2e-2 for O in the BF16 modes, 1e-4 in the
 FP32-output mode, 5e-2 for dQ, dK, dV; tie flags bit-exact against the
-oracle's rule, except rows whose score gap lies within 4 FP32 ulps of eps
-(there a one-ulp difference in S between the MFMA and the oracle's exactly
-rounded dot product may decide the comparison; such rows are counted and
-printed, and are expected to be absent).
+oracle's rule on every row outside the eps band, and equal tie counts up to
+the listed band rows.
+
+The eps band: the oracle defines S through the exactly rounded dot product;
+the MFMA accumulates the 128 (or 64) products in FP32 in groups, which differs
+from it by up to about 8 u sum_f |q_f k_f| (u = 2^-24; a probe of the
+instruction on random and adversarial BF16 data measured at most 7.1, at most
+2.8 without a wide exponent spread).  A row whose top-two gap lies within
+twice that (times the scale) plus four FP32 ulps of eps may be decided either
+way; such rows are listed and counted, everything else must agree.
 """
 from __future__ import annotations
 
@@ -54,11 +60,32 @@ SMALL = [
 ]
 
 
-def _flags_compare(gpu_flags, emu):
-    """Exact flag comparison outside the eps boundary band; returns (mismatch, boundary)."""
-    gap = emu.row_max - emu.row_max2
+def eps_band(q, k, gap, top, scale, eps=1e-3, causal=True, q_pos=None, chunk=512):
+    """Rows whose tie decision the MFMA's FP32 accumulation of the dot product
+    may flip: |gap - eps| <= 2 * 8 u scale max_t sum_f |q_f k_tf| + 4 ulp(top)
+    (see the module docstring).  q: [R, d], k: [N, d] of one slice."""
+    q = np.abs(np.asarray(q, np.float64))
+    k = np.abs(np.asarray(k, np.float64))
+    r = q.shape[0]
+    q_pos = np.arange(r) if q_pos is None else np.asarray(q_pos)
+    amax = np.empty(r)
+    keys = np.arange(k.shape[0])
+    for r0 in range(0, r, chunk):
+        a = q[r0:r0 + chunk] @ k.T
+        if causal:
+            a[keys[None, :] > q_pos[r0:r0 + chunk, None]] = 0.0
+        amax[r0:r0 + chunk] = a.max(axis=1)
+    bound = 2 * 8 * 2.0 ** -24 * scale * amax + 4 * f32_ulp(top)
+    gap = np.asarray(gap, np.float64)
     with np.errstate(invalid="ignore"):
-        band = np.isfinite(gap) & (np.abs(gap - np.float32(1e-3)) <= 4 * f32_ulp(emu.row_max))
+        return np.isfinite(gap) & (np.abs(gap - np.float32(eps)) <= bound)
+
+
+def _flags_compare(gpu_flags, emu, q, k, scale, eps=1e-3, causal=True):
+    """Exact flag comparison outside the eps band; returns (mismatch, band rows)."""
+    gap = emu.row_max - emu.row_max2
+    band = np.stack([eps_band(q[i], k[i], gap[i], emu.row_max[i], scale, eps, causal)
+                     for i in range(q.shape[0])])
     mism = (gpu_flags != emu.flag) & ~band
     return int(mism.sum()), int(band.sum())
 
@@ -130,7 +157,16 @@ def _check_whole_slices(gpu, wl, causal, mode):
         mag = np.sum(np.abs(do[i]) * np.abs(emu.o[i]), axis=-1)
         tol = (1e-5 if mode == "fp32_out" else 2.0 ** -7) * mag + 1e-30
         assert np.all(np.abs(g["delta"].reshape(B * H, N)[i] - want) <= tol)
-    mism, band = _flags_compare(g["flags"].reshape(B * H, N), emu)
+        # and the arithmetic itself: delta against float64 rowsum(dO o O) with
+        # the kernel's own O.  Its FP32 products and d-term sum stay within
+        # (d + 2) 2^-24 of sum |dO| |O|; a dropped or doubled feature would be
+        # off by about 1/d of it.
+        o_k = go[i]
+        want_k = np.sum(do[i].astype(np.float64) * o_k, axis=-1)
+        mag_k = np.sum(np.abs(do[i]) * np.abs(o_k), axis=-1)
+        err_k = np.abs(g["delta"].reshape(B * H, N)[i] - want_k)
+        assert np.all(err_k <= (d + 2) * 2.0 ** -24 * mag_k + 1e-30), float(np.max(err_k / (mag_k + 1e-30)))
+    mism, band = _flags_compare(g["flags"].reshape(B * H, N), emu, q, k, wl.scale, causal=causal)
     if band:
         print(f"  rows in the eps boundary band: {band}")
     assert mism == 0
@@ -237,7 +273,7 @@ def test_other_scales(gpu, scale, mode):
     q, k, v = (x.reshape(B * H, N, d) for x in (inp.q, inp.k, inp.v))
     do = inp.do_for(mode).reshape(B * H, N, d)
     emu = fe.flash_forward(q, k, v, mode=mode, causal=True, scale=scale)
-    mism, _ = _flags_compare(g["flags"].reshape(B * H, N), emu)
+    mism, _ = _flags_compare(g["flags"].reshape(B * H, N), emu, q, k, scale)
     assert mism == 0 and g["flags"].sum() > 0
     for i in range(B * H):
         ref = a64.slice_reference(q[i], k[i], v[i], do[i], causal=True, scale=scale)
@@ -264,8 +300,7 @@ def test_tie_parameters(gpu, beta, eps):
     do = inp.do_for(mode).reshape(B * H, N, d)
     emu = fe.flash_forward(q, k, v, mode=mode, causal=True, scale=wl.scale, beta=beta, eps=eps)
     gap = emu.row_max - emu.row_max2
-    with np.errstate(invalid="ignore"):
-        band = np.isfinite(gap) & (np.abs(gap - np.float32(eps)) <= 4 * f32_ulp(emu.row_max))
+    band = np.stack([eps_band(q[i], k[i], gap[i], emu.row_max[i], wl.scale, eps) for i in range(B * H)])
     gf = g["flags"].reshape(B * H, N)
     assert np.array_equal(gf[~band], emu.flag[~band])
     assert gf.sum() > 0 and np.all(np.isfinite(g["o"]))
@@ -298,11 +333,13 @@ def test_tie_shift_underflow_gives_nan_rows(gpu):
 
 def test_signed_error_gate_config1(gpu):
     """Mean signed O error on tied rows, oriented by the tail (the part of the
-    product not coming from the tied keys), pooled over 4096 seeded repetitions
-    of the single-head tied-rows workload: plain BF16 is biased (<= -5 SE), the
-    tie-aware softmax cuts the bias by at least 10x, FP32 output removes it."""
+    product not coming from the tied keys), pooled over 16384 seeded
+    repetitions of the single-head tied-rows workload: plain BF16 is biased
+    (<= -5 SE), the tie-aware softmax cuts the bias by at least 10x at the
+    lower end of a 95% bootstrap interval (repetitions resampled), FP32 output
+    removes it."""
     wl = workload(1)
-    reps = 4096
+    reps = 16384
     x = generate_reps(wl, reps)
     b = x.q.shape[0]
     q, k, v = (a.reshape(b, 128, 64) for a in (x.q, x.k, x.v))
@@ -313,17 +350,28 @@ def test_signed_error_gate_config1(gpu):
         for i in range(c0, c1):
             o64[i] = a64.fwd_slice(q[i], k[i], v[i], True, wl.scale)[0]
         tau[c0:c1] = st.tail_sums(q[c0:c1], k[c0:c1], v[c0:c1], scale=wl.scale)
-    res = {}
+    res, rows, flags = {}, {}, {}
     for mode in MODES:
         g = gpu.run(x, mode, bwd=False)
         fl = g["flags"].reshape(b, 128)
+        flags[mode] = fl
         res[mode] = st.signed_error(g["o"].reshape(b, 128, 64), o64, tau, fl)
+        rows[mode] = st.row_values(g["o"].reshape(b, 128, 64), o64, tau, fl)
         print(f"[signed error] {mode}: {res[mode]}", flush=True)
-        gpu.record("signed_error_cfg1_x4096", mode,
+    assert np.array_equal(flags["bf16_out"], flags["tie_aware_softmax"])
+    (pt, _, pk), (tt, _, tk) = rows["bf16_out"], rows["tie_aware_softmax"]
+    keep = pk & tk
+    groups = np.nonzero(flags["bf16_out"])[0][keep]      # the repetition of each tied row
+    ci = st.ratio_ci(pt[keep], tt[keep], groups, n_boot=2000, seed=1)
+    print(f"[signed error] plain / tie-aware ratio {ci['ratio']:.1f}, 95% interval "
+          f"[{ci['lo']:.1f}, {ci['hi']:.1f}] over {ci['clusters']} repetitions", flush=True)
+    for mode in MODES:
+        gpu.record("signed_error_cfg1_x16384", mode,
                    {k_: float(v_) for k_, v_ in res[mode].items() if np.isscalar(v_)})
-    p, t, f = res["bf16_out"], res["tie_aware_softmax"], res["fp32_out"]
+    gpu.record("signed_error_cfg1_x16384", "ratio_ci", ci)
+    p, f = res["bf16_out"], res["fp32_out"]
     assert p["tail_mean"] < -5 * p["tail_se"]
-    assert abs(t["tail_mean"]) * 10 <= abs(p["tail_mean"])
+    assert ci["lo"] >= 10.0, ci
     assert abs(f["tail_mean"]) * 100 <= abs(p["tail_mean"])
 
 
@@ -335,15 +383,34 @@ FULL = [
 ]
 
 
+def _oracle_flags_all_slices(q, k, scale, causal=True):
+    """The oracle's untiled tie rule on every (batch, head) slice (rows are
+    independent; slices run on a few threads).  Returns (flags, gap, top)."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        res = list(ex.map(lambda i: fe.tie_top2_untiled(q[i], k[i], causal=causal, scale=scale),
+                          range(q.shape[0])))
+    return tuple(np.stack([r[j] for r in res]) for j in range(3))
+
+
 @pytest.mark.parametrize("wid,modes,slices", FULL, ids=[f"cfg{c[0]}" for c in FULL])
 def test_full_size_configs(gpu, wid, modes, slices):
     """Full-size workloads in the benchmark's launch configuration; whole
-    (batch, head) slices are checked against the float64 reference, and a
-    repeated run must give the same bits."""
+    (batch, head) slices are checked against the float64 reference, the tie
+    flags of every slice against the oracle's untiled rule (bit for bit, equal
+    counts), and a repeated run must give the same bits."""
     wl = workload(wid)
     inp = generate(wl)
     B, H, N, d = wl.b, wl.h, wl.n, wl.d
     q, k, v = (x.reshape(B * H, N, d) for x in (inp.q, inp.k, inp.v))
+    fl_ref, gap, top = _oracle_flags_all_slices(q, k, wl.scale)
+    band = np.zeros_like(fl_ref)
+    near = np.isfinite(gap) & (np.abs(gap.astype(np.float64) - 1e-3) <= 1e-3)   # cheap pre-filter
+    for i in np.unique(np.nonzero(near)[0]):
+        rows = np.nonzero(near[i])[0]
+        band[i, rows] = eps_band(q[i][rows], k[i], gap[i][rows], top[i][rows], wl.scale, q_pos=rows)
+    print(f"[full] cfg{wid}: oracle tie rows {int(fl_ref.sum())} of {fl_ref.size}, rows in the eps band "
+          f"{int(band.sum())}", flush=True)
     for mode in modes:
         print(f"[full] cfg{wid} mode={mode}", flush=True)
         g = gpu.run(inp, mode)
@@ -351,9 +418,20 @@ def test_full_size_configs(gpu, wid, modes, slices):
         g2 = gpu.run(inp, mode)
         for key in ("o", "lse", "flags", "dq", "dk", "dv", "delta"):
             assert np.array_equal(g[key], g2[key]), (mode, key)
+        gf = g["flags"].reshape(B * H, N)
+        mism = gf != fl_ref
+        print(f"  tie rows gpu {int(gf.sum())} oracle {int(fl_ref.sum())}; rows that differ "
+              f"{int(mism.sum())} (of them in the eps band {int((mism & band).sum())})", flush=True)
+        for i, t in np.argwhere(band):
+            print(f"  eps band row (slice {i}, query {t}): gap {float(gap[i, t]):.9g}, oracle flag "
+                  f"{bool(fl_ref[i, t])}, gpu flag {bool(gf[i, t])}", flush=True)
+        assert not (mism & ~band).any(), np.argwhere(mism & ~band)[:10]
+        assert abs(int(gf.sum()) - int(fl_ref.sum())) <= int((mism & band).sum())
         do = inp.do_for(mode).reshape(B * H, N, d)
         rec = {"slices": list(slices), "o": 0.0, "dq": 0.0, "dk": 0.0, "dv": 0.0,
-               "tie_rows_gpu": 0, "tie_rows_oracle": 0, "tie_rows_all_slices_gpu": int(g["flags"].sum())}
+               "tie_rows_gpu": int(gf.sum()), "tie_rows_oracle": int(fl_ref.sum()),
+               "tie_flag_slices": "all", "eps_band_rows": int(band.sum()),
+               "eps_band_rows_differing": int((mism & band).sum())}
         for i in slices:
             ref = a64.slice_reference(q[i], k[i], v[i], do[i], causal=True, scale=wl.scale)
             go = g["o"].reshape(B * H, N, d)[i]
@@ -363,20 +441,6 @@ def test_full_size_configs(gpu, wid, modes, slices):
                 err = st.max_rel_err(g[key].reshape(B * H, N, d)[i], ref[key])
                 rec[key] = max(rec[key], err)
                 assert err <= GRAD_TOL, (key, err)
-            fl_ref = np.zeros(N, bool)
-            band = np.zeros(N, bool)
-            for r0 in range(0, N, 1024):
-                pos = np.arange(r0, min(N, r0 + 1024))
-                fl, _, gap, top = fe.tie_flags_untiled(q[i][pos], k[i], q_pos=pos, scale=wl.scale,
-                                                       return_gap=True)
-                fl_ref[pos] = fl[0]
-                band[pos] = np.abs(gap[0] - np.float32(1e-3)) <= 4 * f32_ulp(top[0])
-            gf = g["flags"].reshape(B * H, N)[i]
-            print(f"  slice {i}: tie rows gpu {int(gf.sum())} oracle {int(fl_ref.sum())} "
-                  f"boundary rows {int(band.sum())}", flush=True)
-            assert np.array_equal(gf[~band], fl_ref[~band])
-            rec["tie_rows_gpu"] += int(gf.sum())
-            rec["tie_rows_oracle"] += int(fl_ref.sum())
         gpu.record("full_size", f"cfg{wid}_{mode}", rec)
 
 
@@ -424,7 +488,7 @@ def test_ragged_large_shapes(gpu, name, wl, slices, mode, causal):
             fl, _, gap, top = fe.tie_flags_untiled(q[i][pos], k[i], causal=causal, q_pos=pos,
                                                    scale=wl.scale, return_gap=True)
             fl_ref[pos] = fl[0]
-            band[pos] = np.abs(gap[0] - np.float32(1e-3)) <= 4 * f32_ulp(top[0])
+            band[pos] = eps_band(q[i][pos], k[i], gap[0], top[0], wl.scale, causal=causal, q_pos=pos)
         gf = g["flags"].reshape(B * H, N)[i]
         assert np.array_equal(gf[~band], fl_ref[~band])
         assert gf.sum() > 0
@@ -495,7 +559,7 @@ def test_long_sequence_sampled_rows(gpu, name, wl, modes):
                 assert err <= GRAD_TOL, (mode, i, key, err)
             fl, _, gap, top = fe.tie_flags_untiled(q[i][q_rows], k[i], q_pos=q_rows, scale=wl.scale,
                                                    return_gap=True)
-            band = np.abs(gap[0] - np.float32(1e-3)) <= 4 * f32_ulp(top[0])
+            band = eps_band(q[i][q_rows], k[i], gap[0], top[0], wl.scale, q_pos=q_rows)
             gf = g["flags"].reshape(B * H, N)[i][q_rows]
             assert np.array_equal(gf[~band], fl[0][~band])
             print(f"  slice {i}: sampled tie rows gpu {int(gf.sum())} oracle {int(fl[0].sum())}", flush=True)
