@@ -214,59 +214,101 @@ def tail_sums(torch, q, k, v, eps=1e-3):
     return torch.matmul(w, v.double())
 
 
+def exact_attention(torch, q, k, v, chunk=2048):
+    """Plain causal attention with scale 1/sqrt(d) in float64 on the GPU (torch
+    operations, slices in chunks): the reference the signed errors are
+    measured against."""
+    B, H, N, d = q.shape
+    out = torch.empty((B, H, N, d), dtype=torch.float64, device=q.device)
+    mask = torch.ones(N, N, dtype=torch.bool, device=q.device).triu(1)
+    qf, kf, vf = (t.reshape(B * H, N, d) for t in (q, k, v))
+    of = out.view(B * H, N, d)
+    for c0 in range(0, B * H, chunk):
+        c1 = min(B * H, c0 + chunk)
+        s = torch.matmul(qf[c0:c1].double(), kf[c0:c1].double().transpose(-1, -2).contiguous()) * (1.0 / d ** 0.5)
+        s = s.masked_fill(mask, float("-inf"))
+        of[c0:c1] = torch.matmul(torch.softmax(s, dim=-1), vf[c0:c1].double())
+    return out
+
+
+def ratio_interval(torch, plain, tie, groups, n_boot=2000, seed=1):
+    """|mean plain| / |mean tie| with a 95% percentile bootstrap interval that
+    resamples whole repetitions (groups), the same ones in both modes."""
+    import numpy as np
+    plain, tie, groups = (t.cpu().numpy() for t in (plain, tie, groups))
+    _, g = np.unique(groups, return_inverse=True)
+    ng = int(g.max()) + 1
+    sp = np.bincount(g, weights=plain, minlength=ng)
+    st_ = np.bincount(g, weights=tie, minlength=ng)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    boots = []
+    for b0 in range(0, n_boot, 100):
+        idx = rng.integers(0, ng, size=(min(100, n_boot - b0), ng))
+        boots.append(np.abs(sp[idx].sum(axis=1)) / np.abs(st_[idx].sum(axis=1)))
+    lo, hi = np.quantile(np.concatenate(boots), [0.025, 0.975])
+    return {"ratio": float(abs(sp.sum()) / abs(st_.sum())), "lo": float(lo), "hi": float(hi),
+            "repetitions": ng}
+
+
 def tail_oriented_stats(torch, pfa, x, to, eps=1e-3):
     """The signed O error on tied rows oriented by the tail, with V ~ N(0,1):
-    per element s = -sign(tau) (O_mode - O_ref), where tau is the part of the
-    row's unnormalised product that does not come from keys within eps of the
-    row maximum, sum over the other keys of exp(S - rm) V (float64).  Plain BF16
-    rounds the sum of the tied V values (P-bar = 1) against the small remainder,
-    so its s is negative; every step is odd in V, so for symmetric V the raw
-    mean is zero in expectation and only this orientation shows the bias.
-    Unit: the row (mean of s over its features); mean, standard error and
-    the plain / tie-aware ratio."""
+    per element s = -sign(tau) (O_mode - O_exact), O_exact the float64
+    attention, tau the part of the row's unnormalised product that does not
+    come from keys within eps of the row maximum, sum over the other keys of
+    exp(S - rm) V (float64).  Plain BF16 rounds the sum of the tied V values
+    (P-bar = 1) against the small remainder, so its s is negative; every step
+    is odd in V, so for symmetric V the raw mean is zero in expectation and
+    only this orientation shows the bias.  Unit: the row (mean of s over its
+    features with tau != 0); mean, standard error across rows, and the plain /
+    tie-aware ratio with a bootstrap interval over repetitions."""
     q, k, v = to(x.q), to(x.k), to(x.v)
-    ref, _, fl = pfa.forward(q, k, v, causal=True, mode="fp32_out")
+    ref = exact_attention(torch, q, k, v)
     B, H, N, d = q.shape
     sign = torch.sign(tail_sums(torch, q, k, v, eps))
-    rows = fl.bool()
-    res = {"shape": f"B{B} H{H} N{N} d{d}", "v": "N(0,1)", "tied_rows": int(rows.sum().item())}
-    for mode in ("bf16_out", "tie_aware_softmax"):
+    _, _, fl = pfa.forward(q, k, v, causal=True, mode="bf16_out")
+    cnt = (sign != 0).double().sum(dim=-1)
+    rows = fl.bool() & (cnt > 0)
+    res = {"shape": f"B{B} H{H} N{N} d{d}", "v": "N(0,1)", "reference": "float64 attention",
+           "tied_rows": int(fl.sum().item()), "rows_with_tail": int(rows.sum().item())}
+    per = {}
+    for mode in ("bf16_out", "tie_aware_softmax", "fp32_out"):
         o, _, _ = pfa.forward(q, k, v, causal=True, mode=mode, flags=False)
-        e = -sign * (o.double() - ref.double())
-        cnt = (sign != 0).double().sum(dim=-1)
-        per_row = (e.sum(dim=-1) / cnt.clamp(min=1))[rows & (cnt > 0)]
+        e = -sign * (o.double() - ref)
+        per_row = (e.sum(dim=-1) / cnt.clamp(min=1))[rows]
+        per[mode] = per_row
         n = per_row.numel()
         res[mode] = {"mean": float(per_row.mean().item()),
                      "se": float(per_row.std().item() / n ** 0.5) if n > 1 else None}
-    res["reduction"] = abs(res["bf16_out"]["mean"]) / max(abs(res["tie_aware_softmax"]["mean"]), 1e-30)
+    groups = torch.nonzero(rows)[:, 0]          # the repetition (batch index) of each row
+    res["reduction"] = ratio_interval(torch, per["bf16_out"], per["tie_aware_softmax"], groups)
     return res
 
 
-def signed_error_stats(torch, pfa, inp, wl):
+def signed_error_stats(torch, pfa, inp, wl, reps=16384):
     """Mean signed O error on tied rows (rows whose tie flag is set), per mode,
-    against the FP32-output forward of the same inputs (accurate to ~1e-6
-    relative, far below the BF16 rounding measured here).  Two inputs: the
-    single-head tied-rows workload (B1 H1 N128 d64, 25% of rows with 2-4 tied
-    maxima and Q x8) pooled over 4096 seeded repetitions with V - 2 -- the
-    pages' mostly negative V, where plain BF16 is biased negative and the
-    tie-aware softmax removes most of it -- and the benchmarked workload itself
-    with V - 2 (there the tied keys carry a small share of each row's weight);
-    and the tail-oriented statistic on the tied-rows workload with N(0,1) V
-    (tail_oriented_stats)."""
+    against the float64 attention of the same inputs: the tail-oriented
+    statistic on the single-head tied-rows workload (B1 H1 N128 d64, 25% of
+    rows with 2-4 tied maxima and Q x8) pooled over `reps` seeded
+    repetitions with N(0,1) V (tail_oriented_stats); and the raw mean with
+    V - 2 -- the pages' mostly negative V, where plain BF16 is biased negative
+    and the tie-aware softmax removes most of it -- on the same pooled
+    workload and on the benchmarked workload itself (there the tied keys carry
+    a small share of each row's weight)."""
     from synth.inputs import generate_reps, workload
     dev = "cuda:0"
     to = lambda x: torch.from_numpy(x).to(dev).to(torch.bfloat16).contiguous()
-    tied = generate_reps(workload(1), 4096)
-    out = {"tied_rows_workload_x4096_tail_oriented": tail_oriented_stats(torch, pfa, tied, to)}
-    for name, x, shape in (("tied_rows_workload_x4096_v_minus_2", tied, "B4096 H1 N128 d64"),
+    tied = generate_reps(workload(1), reps)
+    out = {f"tied_rows_workload_x{reps}_tail_oriented": tail_oriented_stats(torch, pfa, tied, to)}
+    for name, x, shape in ((f"tied_rows_workload_x{reps}_v_minus_2", tied, f"B{reps} H1 N128 d64"),
                            ("benchmarked_workload_v_minus_2", inp, f"B{wl.b} H{wl.h} N{wl.n} d{wl.d}")):
         q, k, v = to(x.q), to(x.k), to(x.v - 2.0)
-        ref, _, fl = pfa.forward(q, k, v, causal=True, mode="fp32_out")
+        ref = exact_attention(torch, q, k, v)
+        _, _, fl = pfa.forward(q, k, v, causal=True, mode="bf16_out")
         rows = fl.bool()
-        res = {"shape": shape, "tied_rows": int(rows.sum().item())}
-        for mode in ("bf16_out", "tie_aware_softmax"):
+        res = {"shape": shape, "tied_rows": int(rows.sum().item()), "reference": "float64 attention"}
+        for mode in ("bf16_out", "tie_aware_softmax", "fp32_out"):
             o, _, _ = pfa.forward(q, k, v, causal=True, mode=mode, flags=False)
-            err = (o.float() - ref)[rows]
+            err = (o.double() - ref)[rows]
             res[mode] = {"mean_signed": float(err.mean().item()), "mean_abs": float(err.abs().mean().item())}
         res["reduction"] = abs(res["bf16_out"]["mean_signed"]) / max(abs(res["tie_aware_softmax"]["mean_signed"]), 1e-30)
         out[name] = res
@@ -276,28 +318,30 @@ def signed_error_stats(torch, pfa, inp, wl):
 
 def signed_error_rows(torch, pfa, inp, mode, eps=1e-3):
     """Mean signed O error of `mode` on the rows its tie flags mark, against the
-    FP32-output forward of the same inputs: raw, and oriented by the tail as in
-    tail_oriented_stats (tail sums one (batch, head) slice at a time).  The row
-    is the unit; returns mean and standard error of each, and the row count."""
+    float64 attention of the same inputs: raw, and oriented by the tail as in
+    tail_oriented_stats (reference and tail sums one (batch, head) slice at a
+    time).  The row is the unit; returns mean and standard error of each, and
+    the row count."""
     dev = "cuda:0"
     to = lambda x: torch.from_numpy(x).to(dev).to(torch.bfloat16).contiguous()
     q, k, v = to(inp.q), to(inp.k), to(inp.v)
     B, H, N, d = q.shape
-    ref, _, fl = pfa.forward(q, k, v, causal=True, mode="fp32_out")
-    o, _, _ = pfa.forward(q, k, v, causal=True, mode=mode, flags=False)
+    o, _, fl = pfa.forward(q, k, v, causal=True, mode=mode)
     raw, tail = [], []
     for b in range(B):
         for h in range(H):
             rows = fl[b, h].bool()
             if not bool(rows.any()):
                 continue
+            sl = lambda t: t[b:b + 1, h:h + 1]
+            ref = exact_attention(torch, sl(q), sl(k), sl(v))[0, 0]
             sign = torch.sign(tail_sums(torch, q[b, h], k[b, h], v[b, h], eps))[rows]
-            e = (o[b, h].double() - ref[b, h].double())[rows]
+            e = (o[b, h].double() - ref)[rows]
             raw.append(e.mean(dim=-1))
             cnt = (sign != 0).double().sum(dim=-1)
             keep = cnt > 0
             tail.append(((-sign * e).sum(dim=-1) / cnt.clamp(min=1))[keep])
-    out = {"tied_rows": int(fl.sum().item())}
+    out = {"tied_rows": int(fl.sum().item()), "reference": "float64 attention"}
     for name, xs in (("raw", raw), ("tail", tail)):
         x = torch.cat(xs) if xs else torch.zeros(0, dtype=torch.float64, device=dev)
         n = x.numel()
@@ -325,8 +369,7 @@ def report(torch, pfa, steps, warmup):
                     "ms_per_step": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
                     "pct_bf16_peak": round(100 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
                     "phases_ms": {k_: round(v_, 4) for k_, v_ in phases.items()}, "tie_rows": ties}
-            if mode != "fp32_out":
-                line["signed_error"] = signed_error_rows(torch, pfa, inp, mode)
+            line["signed_error"] = signed_error_rows(torch, pfa, inp, mode)
             lines.append(line)
         # the CPU leg after the GPU timings: seconds of an idle GPU lower its clocks
         cpu = cpu_baseline(inp, wl, budget_s=4.0)
