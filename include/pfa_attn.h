@@ -70,7 +70,8 @@ enum pfa_status {
   PFA_OK = 0,
   PFA_ERR_INVALID = -1,
   PFA_ERR_UNSUPPORTED = -2,
-  PFA_ERR_HIP = -3
+  PFA_ERR_HIP = -3,
+  PFA_ERR_SCRATCH = -4
 };
 
 /* Parameters of the repeated-maximum-aware softmax (section 3.4.5): beta > 1
@@ -237,6 +238,31 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, cons
 int attn_delta_error(const void* q, const void* k, const void* v, const void* o, const void* dout,
                      const float* lse, float* err, int B, int H, int N, int d, int causal,
                      float scale, int mode, void* stream);
+
+/*
+ * attn_bwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same kernels, with the backward's workspace taken from a static device
+ * array inside the library instead of a caller buffer.  Arguments as attn_bwd
+ * without workspace/workspace_bytes.
+ *
+ * Limit: attn_bwd_workspace_bytes(B, H, N, d, mode) must not exceed
+ * attn_bwd_noalloc_max_bytes() (72 MiB: about 18.8 million rows in the BF16
+ * modes, 290 thousand rows at d = 128 in PFA_FP32_OUT); larger problems
+ * return PFA_ERR_SCRATCH before anything is launched.  Other errors as
+ * attn_bwd.  The call allocates nothing: each GPU holds its own copy of the
+ * array (loaded with the library's code, kept until the process ends), whose
+ * device address is looked up on the first call on that GPU.  Every call on a
+ * GPU shares that GPU's array and leaves its contents behind (the backward
+ * overwrites all it reads): calls that overlap on one GPU (concurrent streams
+ * or host threads) race and give wrong results; serialise them.
+ */
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                     const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int H, int N,
+                     int d, int causal, float scale, int mode, void* stream);
+
+/* Bytes of the static scratch attn_bwd_noalloc uses per GPU. */
+size_t attn_bwd_noalloc_max_bytes(void);
 
 /* Static text for a status code. */
 const char* attn_strerror(int status);

@@ -17,10 +17,11 @@ LIB_PATH = os.path.join(_PKG, "_lib", "libpfa_attn.so")
 
 MODES = {"bf16_out": 0, "fp32_out": 1, "tie_aware_softmax": 2}
 DELTA_SRC = {"do_o": 0, "dp_p": 1, "do_ohp": 2}
-PFA_OK, PFA_ERR_INVALID, PFA_ERR_UNSUPPORTED, PFA_ERR_HIP = 0, -1, -2, -3
+PFA_OK, PFA_ERR_INVALID, PFA_ERR_UNSUPPORTED, PFA_ERR_HIP, PFA_ERR_SCRATCH = 0, -1, -2, -3, -4
 EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_prep", "attn_bwd_dkdv", "attn_bwd_dq",
             "attn_bwd_delta", "attn_bwd_ex", "attn_delta_error", "attn_fwd_heads", "attn_fwd_diag",
-            "attn_bwd_workspace_bytes", "attn_strerror", "attn_version")
+            "attn_bwd_workspace_bytes", "attn_strerror", "attn_version", "attn_bwd_noalloc",
+            "attn_bwd_noalloc_max_bytes")
 
 
 class TieOpts(ctypes.Structure):
@@ -73,6 +74,10 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd_heads.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp,
                                      ctypes.POINTER(TieOpts), vp]
         L.attn_fwd_heads.restype = i
+        L.attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+        L.attn_bwd_noalloc.restype = i
+        L.attn_bwd_noalloc_max_bytes.argtypes = []
+        L.attn_bwd_noalloc_max_bytes.restype = ctypes.c_size_t
         L.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
         L.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.attn_strerror.argtypes = [i]
@@ -219,6 +224,30 @@ def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, delta=None, causal=Tr
         _check(lib().attn_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
                                  _ptr(dk), _ptr(dv), _ptr(delta), _ptr(workspace), nbytes, B, H, N,
                                  d, int(bool(causal)), scale, mid, src, _stream(stream)))
+
+
+def attn_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, delta=None, causal=True, scale=None,
+                     mode="bf16_out", stream=None):
+    """attn_bwd with the workspace in the library's static device scratch
+    (see attn_bwd_noalloc in pfa_attn.h): nothing is allocated."""
+    B, H, N, d = q.shape
+    mid = _mode_id(mode)
+    io = torch.float32 if mid == 1 else torch.bfloat16
+    for name, t in (("q", q), ("k", k), ("v", v), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _expect(t, name, torch.bfloat16, (B, H, N, d))
+    _expect(o, "o", io, (B, H, N, d))
+    _expect(dout, "dout", io, (B, H, N, d))
+    _expect(lse, "lse", torch.float32, (B, H, N))
+    if delta is not None:
+        _expect(delta, "delta", torch.float32, (B, H, N))
+    scale = 1.0 / d ** 0.5 if scale is None else float(scale)
+    _check(lib().attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                                  _ptr(dk), _ptr(dv), _ptr(delta), B, H, N, d, int(bool(causal)), scale,
+                                  mid, _stream(stream)))
+
+
+def attn_bwd_noalloc_max_bytes() -> int:
+    return int(lib().attn_bwd_noalloc_max_bytes())
 
 
 def _ws(workspace):

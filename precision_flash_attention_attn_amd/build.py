@@ -17,7 +17,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB_DIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIB_DIR, "libpfa_attn.so")
 
-SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_bwd_dq.hip", "attn_bwd_delta.hip", "attn_api.cpp"]
+SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_bwd_dq.hip", "attn_bwd_delta.hip", "attn_noalloc.hip",
+           "attn_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

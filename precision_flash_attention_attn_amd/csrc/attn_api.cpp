@@ -283,6 +283,43 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   return status_of(e);
 }
 
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                     const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int H, int N,
+                     int d, int causal, float scale, int mode, void* stream) {
+  // every argument check before the first HIP call
+  const int st = check_common(B, H, N, d, scale, mode);
+  if (st != PFA_OK) return st;
+  if (attn_bwd_workspace_bytes(B, H, N, d, mode) > pfa::kNoallocScratchBytes) return PFA_ERR_SCRATCH;
+  if (delta && !aligned4(delta)) return PFA_ERR_INVALID;
+  if (!ok16(q) || !ok16(k) || !ok16(v) || !ok16(o) || !ok16(dout) || !ok16(dq) || !ok16(dk) ||
+      !ok16(dv))
+    return PFA_ERR_INVALID;
+  if (!lse || !aligned4(lse)) return PFA_ERR_INVALID;
+  void* ws = nullptr;
+  const int sst = pfa::noalloc_scratch(stream, &ws);
+  if (sst != PFA_OK) return sst;
+  pfa::BwdArgs a;
+  // the same workspace layout as attn_bwd, in the scratch
+  const int st2 = bwd_args(a, ws, pfa::kNoallocScratchBytes, delta, B, H, N, d, causal, scale, mode);
+  if (st2 != PFA_OK) return st2;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = pfa::launch_bwd_prep(a, s);
+  if (e == hipSuccess) e = pfa::launch_bwd_dkdv(a, s);
+  if (e == hipSuccess) e = pfa::launch_bwd_dq(a, s);
+  return status_of(e);
+}
+
+size_t attn_bwd_noalloc_max_bytes(void) { return pfa::kNoallocScratchBytes; }
+
 int attn_bwd_delta(const void* q, const void* k, const void* v, const void* o, const void* dout,
                    const float* lse, float* delta, void* workspace, size_t workspace_bytes, int B,
                    int H, int N, int d, int causal, float scale, int mode, int delta_src,
@@ -373,6 +410,8 @@ const char* attn_strerror(int status) {
     case PFA_ERR_INVALID: return "invalid argument";
     case PFA_ERR_UNSUPPORTED: return "unsupported configuration (head dimension must be 64 or 128)";
     case PFA_ERR_HIP: return "HIP launch failure";
+    case PFA_ERR_SCRATCH:
+      return "workspace larger than the static scratch of attn_bwd_noalloc (see attn_bwd_noalloc_max_bytes)";
     default: return "unknown status";
   }
 }

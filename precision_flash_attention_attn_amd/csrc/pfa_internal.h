@@ -58,6 +58,14 @@ inline size_t bwd_dout16_bytes(size_t rows, int d, int mode) {
   return mode == kFp32Out ? align256(rows * (size_t)d * 2) : 0;
 }
 
+// Size of the static device scratch of attn_bwd_noalloc (per device).
+constexpr size_t kNoallocScratchBytes = size_t(72) << 20;
+
+// Device address of the static scratch on the stream's device (the current
+// device for a NULL stream), looked up once per device.  Returns a PFA_*
+// status.
+int noalloc_scratch(void* stream, void** ptr);
+
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 // The backward in three kernels on one stream: delta = rowsum(dO o O); dK and
 // dV; dQ.

@@ -193,3 +193,24 @@ def test_diag_forward_requires_the_count_buffer(L):
     assert f(FAKE + 2) == inv
     assert f(FAKE, one=FAKE + 4) == inv   # o_one must be 16-byte aligned
 
+
+def test_noalloc_backward_rejects_problems_beyond_its_scratch(L):
+    """attn_bwd_noalloc: sizes whose workspace exceeds the static scratch return
+    PFA_ERR_SCRATCH, other bad arguments PFA_ERR_INVALID, all before any HIP
+    call (every case here fails a check; none launches)."""
+    mx = L.attn_bwd_noalloc_max_bytes()
+    assert mx == 72 << 20
+    args = lambda N, mode=1, d=128, dq=FAKE, lse=FAKE: (FAKE, FAKE, FAKE, FAKE, FAKE, lse, dq, FAKE, FAKE, None,
+                                                       1, 1, N, d, 1, 0.088, mode, None)
+    # FP32-output mode at d = 128: 4 + 256 bytes of workspace per row
+    rows_fit = mx // 260
+    assert L.attn_bwd_workspace_bytes(1, 1, rows_fit + 4096, 128, 1) > mx
+    assert L.attn_bwd_noalloc(*args(rows_fit + 4096)) == bnd.PFA_ERR_SCRATCH
+    assert L.attn_bwd_noalloc(*args(1 << 21)) == bnd.PFA_ERR_SCRATCH
+    # BF16 modes need only the delta vector: 2^21 rows fit, so these fail on pointers
+    assert L.attn_bwd_noalloc(*args(1 << 21, mode=0, dq=FAKE + 2)) == bnd.PFA_ERR_INVALID
+    assert L.attn_bwd_noalloc(*args(128, mode=0, lse=None)) == bnd.PFA_ERR_INVALID
+    assert L.attn_bwd_noalloc(*args(0, mode=0)) == bnd.PFA_ERR_INVALID
+    assert L.attn_bwd_noalloc(*args(128, mode=5)) == bnd.PFA_ERR_INVALID
+    assert L.attn_bwd_noalloc(*args(128, d=96)) == bnd.PFA_ERR_UNSUPPORTED
+    assert b"scratch" in L.attn_strerror(bnd.PFA_ERR_SCRATCH)
