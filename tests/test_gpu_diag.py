@@ -95,3 +95,59 @@ def test_pbar_one_count_natural_ties(gpu):
     print(f"  rows that differ {int(np.sum(got != emu.n_pbar_one))}; totals {got.sum()} vs "
           f"{emu.n_pbar_one.sum()}", flush=True)
     assert np.array_equal(got, emu.n_pbar_one)
+
+
+def test_signed_error_by_number_of_pbar_one(gpu):
+    """The pages trace the negative bias of plain BF16 to rows with more than
+    one P-bar = 1 (section 3.4.4, Claim 3: the sum of the tied V values
+    overflows the significand and the tail's sticky bits round it up in
+    magnitude).  With the diagnostic count, on the tied-rows workload pooled
+    over 4096 repetitions (V ~ N(0,1), errors oriented by the tail as in the
+    signed-error gate): in plain BF16, rows with two or more P-bar = 1 entries
+    carry a negative mean error (< -5 SE), while rows with exactly one carry a
+    positive one (> +5 SE: a single BF16-exact V plus a tail smaller than half
+    an ulp rounds the tail away).  In the tie-aware mode the rows with repeated
+    P-bar = 1 are gone but for a few whose shift still rounds to 1, and no
+    group is below -5 SE.  o_one gives the part of O those entries carry."""
+    import precision_flash_attention_attn_amd as pfa
+    from oracle import attention64 as a64
+    from oracle import stats as st
+    from synth.inputs import generate_reps
+    wl = workload(1)
+    reps = 4096
+    x = generate_reps(wl, reps)
+    b = x.q.shape[0]
+    q3, k3, v3 = (a.reshape(b, 128, 64) for a in (x.q, x.k, x.v))
+    o64 = np.stack([a64.fwd_slice(q3[i], k3[i], v3[i], True, wl.scale)[0] for i in range(b)])
+    tau = st.tail_sums(q3, k3, v3, scale=wl.scale)
+    q, k, v = gpu.dev_bf16(x.q), gpu.dev_bf16(x.k), gpu.dev_bf16(x.v)
+    res = {}
+    for mode in ("bf16_out", "tie_aware_softmax"):
+        o = torch.empty_like(q)
+        lse = torch.empty((b, 1, 128), device=q.device, dtype=torch.float32)
+        fl = torch.empty((b, 1, 128), device=q.device, dtype=torch.int32)
+        cnt = torch.empty_like(fl)
+        one = torch.empty(q.shape, device=q.device, dtype=torch.float32)
+        pfa.attn_fwd_diag(q, k, v, o, lse, fl, cnt, one, mode=mode)
+        torch.cuda.synchronize()
+        go = gpu.host(o).reshape(b, 128, 64)
+        n1 = cnt.cpu().numpy().reshape(b, 128)
+        share = np.abs(gpu.host(one).reshape(b, 128, 64)).sum(-1) / (np.abs(go).sum(-1) + 1e-30)
+        tail, _, kept = st.row_values(go, o64, tau, np.ones((b, 128), bool))
+        n1, share = n1.reshape(-1), share.reshape(-1)
+        for name, sel in (("repeated", n1 >= 2), ("single", n1 == 1), ("none", n1 == 0)):
+            vals = tail[sel & kept]
+            if len(vals) < 2:
+                continue
+            r = {"rows": int(len(vals)), "mean": float(vals.mean()), "se": float(vals.std(ddof=1) / np.sqrt(len(vals))),
+                 "share_of_o_from_pbar_one": float(share[sel & kept].mean())}
+            res[(mode, name)] = r
+            print(f"[pbar=1 split] {mode} {name}: {r}", flush=True)
+            gpu.record("signed_error_by_pbar_one_cfg1_x4096", f"{mode}_{name}", r)
+    rep_, one_ = res[("bf16_out", "repeated")], res[("bf16_out", "single")]
+    assert rep_["mean"] < -5 * rep_["se"]
+    assert one_["mean"] > 5 * one_["se"]
+    for (mode, name), r in res.items():
+        if mode == "tie_aware_softmax":
+            assert r["mean"] > -5 * r["se"], (name, r)
+    assert res[("tie_aware_softmax", "repeated")]["rows"] < 0.2 * rep_["rows"]
