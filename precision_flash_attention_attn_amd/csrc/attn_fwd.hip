@@ -94,6 +94,68 @@ __device__ __forceinline__ void map_block(int bid, int BH, int nqb, int& bh, int
 // d >= one_thr.  The same entries are
 // counted in every mode (in the FP32-output mode they enter the product as
 // hi + lo within 2^-9 of 1).
+// Largest element of x: one v_max3_f32 per two elements.
+template <int N>
+struct MaxAll {
+  static __device__ __forceinline__ float run(const float (&x)[N]) {
+    float r = x[0];
+    int i = 1;
+#pragma unroll
+    for (; i + 1 < N; i += 2) r = __builtin_fmaxf(__builtin_fmaxf(r, x[i]), x[i + 1]);
+    if (i < N) r = __builtin_fmaxf(r, x[i]);
+    return r;
+  }
+};
+
+// Largest (t1) and second largest (t2) element of x, as a multiset: t2 = t1
+// when the maximum occurs twice.  Each group of three gives its maximum
+// (v_max3_f32) and median (v_med3_f32); the second largest element is then
+// the larger of the largest median and the second largest group maximum,
+// found the same way one level up.  About 1.3 instructions per element
+// instead of 2 for a running pair.  hv, lv: +inf and -inf (see FwdParams).
+template <int N>
+struct Top2 {
+  static constexpr int G = N / 3, R = N % 3, M = G + (R ? 1 : 0), NB = G + (R == 2 ? 1 : 0);
+  static __device__ __forceinline__ void run(const float (&x)[N], float& t1, float& t2, float hv, float lv) {
+    float a[M], b[NB];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      a[g] = __builtin_fmaxf(__builtin_fmaxf(x[3 * g], x[3 * g + 1]), x[3 * g + 2]);
+      b[g] = med3(x[3 * g], x[3 * g + 1], x[3 * g + 2]);
+    }
+    if (R == 2) {
+      a[G] = med3(x[N - 2], x[N - 1], hv);
+      b[G] = med3(x[N - 2], x[N - 1], lv);
+    } else if (R == 1) {
+      a[G] = x[N - 1];
+    }
+    float s2;
+    Top2<M>::run(a, t1, s2, hv, lv);
+    t2 = __builtin_fmaxf(s2, MaxAll<NB>::run(b));
+  }
+};
+template <>
+struct Top2<1> {
+  static __device__ __forceinline__ void run(const float (&x)[1], float& t1, float& t2, float, float lv) {
+    t1 = x[0];
+    t2 = lv;
+  }
+};
+template <>
+struct Top2<2> {
+  static __device__ __forceinline__ void run(const float (&x)[2], float& t1, float& t2, float hv, float lv) {
+    t1 = med3(x[0], x[1], hv);
+    t2 = med3(x[0], x[1], lv);
+  }
+};
+template <>
+struct Top2<3> {
+  static __device__ __forceinline__ void run(const float (&x)[3], float& t1, float& t2, float, float) {
+    t1 = __builtin_fmaxf(__builtin_fmaxf(x[0], x[1]), x[2]);
+    t2 = med3(x[0], x[1], x[2]);
+  }
+};
+
 template <int D, int MODE, bool CAUSAL, bool FLAGS, bool DIAG, bool WIDE>
 struct FwdKernel {
   // WIDE (d = 128 with fewer than 32 (batch, head) slices): 8 waves over 256
@@ -204,14 +266,14 @@ struct FwdKernel {
     // not use the rounded S values it is defined on.
 #pragma clang fp contract(off)
     const float hv = p.pinf, lv = p.ninf;
-    float t1 = kNegInf, t2 = kNegInf;
+    float x[16 * KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (FLAGS) t2 = med3(t1, t2, s[kb][r]);
-        t1 = med3(t1, s[kb][r], hv);
-      }
+      for (int r = 0; r < 16; ++r) x[16 * kb + r] = s[kb][r];
+    float t1, t2 = kNegInf;
+    if (FLAGS) Top2<16 * KB>::run(x, t1, t2, hv, lv);
+    else t1 = MaxAll<16 * KB>::run(x);
     // combine the two lane halves that share a query
     float a1, b1;
     pair32(t1, a1, b1);
