@@ -1,7 +1,8 @@
 """Benchmark: attention forward + backward throughput on one MI355X.
 
-One step = attn_fwd + the three backward kernels (attn_bwd_prep, attn_bwd_dkdv,
-attn_bwd_dq) over one batch of synthetic inputs already resident in HBM:
+One step = attn_fwd + the two backward kernels as attn_bwd runs them
+(attn_bwd_dq_delta, which also forms delta = rowsum(dO o O), then
+attn_bwd_dkdv) over one batch of synthetic inputs already resident in HBM:
 the long-context workload B=1, H=16, N=8192, d=128, causal (the headline
 throughput configuration).  Throughput counts the algorithmic FLOPs
 7 * B * H * N^2 * d (forward: S = QK^T and P-bar V; backward: the S recompute,
@@ -137,14 +138,15 @@ def run_mode(torch, pfa, inp, wl, mode, steps, warmup, candidates=("fwd", "bwd_d
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
     ws = torch.empty(pfa.attn_bwd_workspace_bytes(B, H, N, d, mode), device=dev, dtype=torch.uint8)
     stream = torch.cuda.current_stream()
-    stages = ("fwd", "bwd_prep", "bwd_dkdv", "bwd_dq")
+    # the backward as attn_bwd runs it: dQ (which also forms delta and, for an
+    # FP32 dO, its BF16 copy), then dK and dV
+    stages = ("fwd", "bwd_dq", "bwd_dkdv")
     calls = {
         "fwd": lambda: pfa.attn_fwd(q, k, v, o, lse, flags, causal=True, mode=mode, stream=stream),
-        "bwd_prep": lambda: pfa.attn_bwd_prep(o, do, ws, mode=mode, stream=stream),
+        "bwd_dq": lambda: pfa.attn_bwd_dq_delta(q, k, v, o, do, lse, dq, ws, causal=True, mode=mode,
+                                                stream=stream),
         "bwd_dkdv": lambda: pfa.attn_bwd_dkdv(q, k, v, do, lse, dk, dv, ws, causal=True, mode=mode,
                                               stream=stream),
-        "bwd_dq": lambda: pfa.attn_bwd_dq(q, k, v, do, lse, dq, ws, causal=True, mode=mode,
-                                          stream=stream),
     }
     event = lambda: torch.cuda.Event(enable_timing=True)
     for _ in range(warmup):
@@ -352,7 +354,7 @@ def signed_error_rows(torch, pfa, inp, mode, eps=1e-3):
 
 def report(torch, pfa, steps, warmup):
     """One JSON line per workload and mode (the five synthetic workloads, each
-    in the modes it lists): wall time of a fwd+bwd step (the four kernels,
+    in the modes it lists): wall time of a fwd+bwd step (the three kernels,
     inputs resident), TFLOP/s against the algorithmic count, tie rows, the
     signed O error on tied rows (BF16 modes; the FP32-output forward is the
     reference), and the float64 oracle's time on the host for the whole

@@ -172,9 +172,10 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              int causal, float scale, int mode, void* stream);
 
 /*
- * The backward in its three kernels, for callers that schedule or time them
- * separately.  attn_bwd runs exactly these three on one stream; running them
- * in this order on one stream gives the same result.
+ * The backward in stages, for callers that schedule or time them separately.
+ * Two orders give bit for bit the result of attn_bwd, each on one stream:
+ *   attn_bwd_prep, attn_bwd_dkdv, attn_bwd_dq   (three kernels), or
+ *   attn_bwd_dq_delta, attn_bwd_dkdv            (two kernels; what attn_bwd runs).
  *
  * Stage 1, attn_bwd_prep: delta = rowsum(dO o O) in FP32 -- the term the
  * pages single out as computed apart in the backward (section 3.4.2) -- into
@@ -198,6 +199,17 @@ int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
 int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                 const float* delta, void* dq, void* workspace, size_t workspace_bytes, int B, int H,
                 int N, int d, int causal, float scale, int mode, void* stream);
+
+/* Stages 1 and 3 in one kernel, attn_bwd_dq_delta: dQ as attn_bwd_dq, with
+ * delta = rowsum(dO o O) (section 3.4.2) formed per query row on the way --
+ * summed in the order attn_bwd_prep uses, so the value is bit for bit the
+ * same -- and written to `delta` (or the workspace when delta is NULL); in
+ * PFA_FP32_OUT also the BF16 copy of dO in the workspace.  attn_bwd_dkdv with
+ * the same delta and workspace, after it on the same stream, completes the
+ * backward.  o, dout: BF16 (FP32 in PFA_FP32_OUT).  Errors as attn_bwd. */
+int attn_bwd_dq_delta(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                      const float* lse, void* dq, float* delta, void* workspace, size_t workspace_bytes,
+                      int B, int H, int N, int d, int causal, float scale, int mode, void* stream);
 
 /*
  * Where the backward takes delta from: the isolation experiments of section

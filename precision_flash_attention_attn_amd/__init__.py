@@ -8,7 +8,7 @@ include/pfa_attn.h; this package is the thin Python binding.
 """
 from ._binding import (DELTA_SRC, LIB_PATH, MODES, AttnError, attn_bwd,  # noqa: F401
                        attn_bwd_noalloc, attn_bwd_noalloc_max_bytes,
-                       attn_bwd_delta, attn_bwd_dkdv, attn_bwd_dq, attn_bwd_prep,
+                       attn_bwd_delta, attn_bwd_dkdv, attn_bwd_dq, attn_bwd_dq_delta, attn_bwd_prep,
                        attn_bwd_workspace_bytes, attn_delta_error, attn_fwd, attn_fwd_diag, attn_fwd_heads,
                        attn_strerror, backward, forward, forward_heads, lib)
 

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "_lib", "libpfa_attn.so")
 MODES = {"bf16_out": 0, "fp32_out": 1, "tie_aware_softmax": 2}
 DELTA_SRC = {"do_o": 0, "dp_p": 1, "do_ohp": 2}
 PFA_OK, PFA_ERR_INVALID, PFA_ERR_UNSUPPORTED, PFA_ERR_HIP, PFA_ERR_SCRATCH = 0, -1, -2, -3, -4
-EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_prep", "attn_bwd_dkdv", "attn_bwd_dq",
+EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_prep", "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_dq_delta",
             "attn_bwd_delta", "attn_bwd_ex", "attn_delta_error", "attn_fwd_heads", "attn_fwd_diag",
             "attn_bwd_workspace_bytes", "attn_strerror", "attn_version", "attn_bwd_noalloc",
             "attn_bwd_noalloc_max_bytes")
@@ -60,6 +60,9 @@ def lib() -> ctypes.CDLL:
         L.attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                   i, i, i, i, i, f, i, vp]
         L.attn_bwd_dq.restype = i
+        L.attn_bwd_dq_delta.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                        i, i, i, i, i, f, i, vp]
+        L.attn_bwd_dq_delta.restype = i
         L.attn_bwd_delta.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                      i, i, i, i, i, f, i, i, vp]
         L.attn_bwd_delta.restype = i
@@ -343,6 +346,20 @@ def attn_bwd_dq(q, k, v, dout, lse, dq, workspace, delta=None, causal=True, scal
     _check(lib().attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(delta),
                              _ptr(dq), wp, wn, B, H, N, d, int(bool(causal)), scale, mid,
                              _stream(stream)))
+
+
+def attn_bwd_dq_delta(q, k, v, o, dout, lse, dq, workspace, delta=None, causal=True, scale=None,
+                      mode="bf16_out", stream=None):
+    """Backward stages 1 and 3 in one kernel: dQ, delta and (FP32 output) the
+    BF16 dO copy; attn_bwd_dkdv afterwards completes the backward."""
+    B, H, N, d, mid = _stage_args(q, k, v, dout, lse, delta, mode)
+    _expect(o, "o", torch.float32 if mid == 1 else torch.bfloat16, (B, H, N, d))
+    _expect(dq, "dq", torch.bfloat16, (B, H, N, d))
+    scale = 1.0 / d ** 0.5 if scale is None else float(scale)
+    wp, wn = _ws(workspace)
+    _check(lib().attn_bwd_dq_delta(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                                   _ptr(delta), wp, wn, B, H, N, d, int(bool(causal)), scale, mid,
+                                   _stream(stream)))
 
 
 # ---- conveniences that allocate with torch and call the entry points above ----

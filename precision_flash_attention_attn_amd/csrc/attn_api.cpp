@@ -256,6 +256,24 @@ int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout, c
   return status_of(pfa::launch_bwd_dq(a, static_cast<hipStream_t>(stream)));
 }
 
+int attn_bwd_dq_delta(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                      const float* lse, void* dq, float* delta, void* workspace, size_t workspace_bytes,
+                      int B, int H, int N, int d, int causal, float scale, int mode, void* stream) {
+  pfa::BwdArgs a;
+  const int st = bwd_args(a, workspace, workspace_bytes, delta, B, H, N, d, causal, scale, mode);
+  if (st != PFA_OK) return st;
+  if (!ok16(q) || !ok16(k) || !ok16(v) || !ok16(o) || !ok16(dout) || !ok16(dq)) return PFA_ERR_INVALID;
+  if (!lse || !aligned4(lse)) return PFA_ERR_INVALID;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  return status_of(pfa::launch_bwd_dq_delta(a, static_cast<hipStream_t>(stream)));
+}
+
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
              const float* lse, void* dq, void* dk, void* dv, float* delta, void* workspace,
              size_t workspace_bytes, int B, int H, int N, int d, int causal, float scale, int mode,
@@ -277,9 +295,10 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   a.dk = dk;
   a.dv = dv;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = pfa::launch_bwd_prep(a, s);
+  // dQ first: it also forms delta (and the BF16 dO of the FP32-output mode)
+  // for the dK/dV kernel, which saves the pre-pass over O and dO
+  hipError_t e = pfa::launch_bwd_dq_delta(a, s);
   if (e == hipSuccess) e = pfa::launch_bwd_dkdv(a, s);
-  if (e == hipSuccess) e = pfa::launch_bwd_dq(a, s);
   return status_of(e);
 }
 
@@ -312,9 +331,10 @@ int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
   a.dk = dk;
   a.dv = dv;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = pfa::launch_bwd_prep(a, s);
+  // dQ first: it also forms delta (and the BF16 dO of the FP32-output mode)
+  // for the dK/dV kernel, which saves the pre-pass over O and dO
+  hipError_t e = pfa::launch_bwd_dq_delta(a, s);
   if (e == hipSuccess) e = pfa::launch_bwd_dkdv(a, s);
-  if (e == hipSuccess) e = pfa::launch_bwd_dq(a, s);
   return status_of(e);
 }
 
@@ -373,8 +393,13 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, cons
   a.dv = dv;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
-  if (delta_src == PFA_DELTA_DO_O || mode == PFA_FP32_OUT) e = pfa::launch_bwd_prep(a, s);
-  if (e == hipSuccess && delta_src != PFA_DELTA_DO_O) e = pfa::launch_bwd_delta(a, delta_src, a.delta, s);
+  if (delta_src == PFA_DELTA_DO_O) {
+    e = pfa::launch_bwd_dq_delta(a, s);
+    if (e == hipSuccess) e = pfa::launch_bwd_dkdv(a, s);
+    return status_of(e);
+  }
+  if (mode == PFA_FP32_OUT) e = pfa::launch_bwd_prep(a, s);
+  if (e == hipSuccess) e = pfa::launch_bwd_delta(a, delta_src, a.delta, s);
   if (e == hipSuccess) e = pfa::launch_bwd_dkdv(a, s);
   if (e == hipSuccess) e = pfa::launch_bwd_dq(a, s);
   return status_of(e);

@@ -28,12 +28,19 @@ struct DqParams {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
-  const uint16_t* dout;   // BF16 dO (the pre-pass copy in the FP32-output mode)
+  const uint16_t* dout;   // BF16 dO (the pre-pass copy in the FP32-output mode); unused with DELTA
   const float* lse;
-  const float* delta;
+  float* delta;           // read (without DELTA) or written (DELTA)
   uint16_t* dq;
   int BH, N, n_qblocks;
   float scale;
+  // DELTA: the kernel forms delta = rowsum(dO o O) itself from O and the
+  // caller's dO (FP32 both when f32io, else BF16) and writes it to `delta`;
+  // with f32io it also writes the BF16 copy of dO that the dK/dV kernel reads.
+  const void* o;
+  const void* dout_in;
+  uint16_t* dout16;
+  int f32io;
 };
 
 __device__ __forceinline__ int sigma32(int i) {
@@ -52,7 +59,7 @@ __device__ __forceinline__ void map_block(int bid, int BH, int nqb, int& bh, int
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DELTA>
 struct DqKernel {
   static constexpr int BM = 128, BN = 64, NT = 256;
   static constexpr int CH = D / 8;
@@ -167,6 +174,83 @@ struct DqKernel {
     }
   }
 
+  // DELTA: dO of this lane's query into doreg (converted to BF16 from an FP32
+  // dO, whose BF16 copy is stored as well) and delta = rowsum(dO o O), summed
+  // in the order of the pre-pass kernel -- a partial sum per 8-feature chunk,
+  // then a butterfly over the chunks (c + c^8, then ^4, ^2, ^1 at d = 128) --
+  // so that it is bit for bit the pre-pass's delta.  The lane holds chunks
+  // 2c + hi: every butterfly step but the last pairs two of its own chunks.
+  __device__ __forceinline__ float own_delta(bool valid) {
+    float part[DC];
+    const size_t row = base + (size_t)myq * D;
+    // all of the lane's loads first, then the sums: one wait for the lot
+    if (p.f32io) {
+      f32x4 oa[DC][2], da[DC][2];
+      if (valid) {
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+          const int col = (2 * c + hi) * 8;
+          const f32x4* op = reinterpret_cast<const f32x4*>(static_cast<const float*>(p.o) + row + col);
+          const f32x4* dp = reinterpret_cast<const f32x4*>(static_cast<const float*>(p.dout_in) + row + col);
+          oa[c][0] = op[0];
+          oa[c][1] = op[1];
+          da[c][0] = dp[0];
+          da[c][1] = dp[1];
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < DC; ++c) oa[c][0] = oa[c][1] = da[c][0] = da[c][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc += oa[c][0][i] * da[c][0][i];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc += oa[c][1][i] * da[c][1][i];
+        part[c] = acc;
+        const f32x4 d0 = da[c][0], d1 = da[c][1];
+        doreg[c] = u32x4{pack_bf16(d0[0], d0[1]), pack_bf16(d0[2], d0[3]), pack_bf16(d1[0], d1[1]),
+                         pack_bf16(d1[2], d1[3])};
+        if (valid) *reinterpret_cast<u32x4*>(p.dout16 + row + (2 * c + hi) * 8) = doreg[c];
+      }
+    } else {
+      u32x4 ov[DC];
+      if (valid) {
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+          const int col = (2 * c + hi) * 8;
+          ov[c] = ldg_b128(static_cast<const uint16_t*>(p.o) + row + col);
+          doreg[c] = ldg_b128(static_cast<const uint16_t*>(p.dout_in) + row + col);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < DC; ++c) ov[c] = doreg[c] = u32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc += bf16lo_to_f32(ov[c][i]) * bf16lo_to_f32(doreg[c][i]);
+          acc += bf16hi_to_f32(ov[c][i]) * bf16hi_to_f32(doreg[c][i]);
+        }
+        part[c] = acc;
+      }
+    }
+#pragma unroll
+    for (int m = DC / 2; m >= 1; m >>= 1) {
+      float nxt[DC];
+#pragma unroll
+      for (int c = 0; c < DC; ++c) nxt[c] = part[c] + part[c ^ m];
+#pragma unroll
+      for (int c = 0; c < DC; ++c) part[c] = nxt[c];
+    }
+    const float dl = part[0] + xchg32(part[0]);
+    if (valid && hi == 0) p.delta[(size_t)bh * N + myq] = dl;
+    return dl;
+  }
+
   template <int BUF, bool MASK>
   __device__ __forceinline__ void step(int j, int n_tiles) {
     if (j + 1 < n_tiles) issue_tile<1 - BUF>(j + 1);
@@ -190,21 +274,25 @@ struct DqKernel {
     qw0 = q0 + 32 * w;
     myq = qw0 + (lane & 31);
     const bool valid = myq < N;
-
-#pragma unroll
-    for (int c = 0; c < DC; ++c) {
-      const int col = (2 * c + hi) * 8;
-      qreg[c] = valid ? ldg_b128(Q + (size_t)myq * D + col) : u32x4{0, 0, 0, 0};
-      doreg[c] = valid ? ldg_b128(p.dout + base + (size_t)myq * D + col) : u32x4{0, 0, 0, 0};
-    }
-    lse2 = valid ? p.lse[(size_t)bh * N + myq] * kLog2e : __builtin_inff();
-    dlt = valid ? p.delta[(size_t)bh * N + myq] : 0.f;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int slot = (w * LOADS + i) * 64 + lane;
       const int row = slot / CH, pchunk = slot % CH;
       voff[i] = (row * D + (pchunk ^ swz_pattern<CH>(row)) * 8) * 2;
     }
+    // the first K/V tile's loads go out first: the wait for this lane's rows
+    // (and, with DELTA, for O before delta is summed) then overlaps them
+    issue_tile<0>(0);
+
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+      const int col = (2 * c + hi) * 8;
+      qreg[c] = valid ? ldg_b128(Q + (size_t)myq * D + col) : u32x4{0, 0, 0, 0};
+      if (!DELTA) doreg[c] = valid ? ldg_b128(p.dout + base + (size_t)myq * D + col) : u32x4{0, 0, 0, 0};
+    }
+    if (DELTA) dlt = own_delta(valid);
+    else dlt = valid ? p.delta[(size_t)bh * N + myq] : 0.f;
+    lse2 = valid ? p.lse[(size_t)bh * N + myq] * kLog2e : __builtin_inff();
     const int krow = sigma32(lane & 31);
 #pragma unroll
     for (int c = 0; c < DC; ++c) kofs[c] = swz<CH>(krow, 2 * c + hi);
@@ -220,7 +308,6 @@ struct DqKernel {
 
     const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
     const int n_tiles = (kv_end + BN - 1) / BN;
-    issue_tile<0>(0);
     wait_all_and_barrier();
     // Leading tiles that need no mask for any wave of the workgroup (all keys
     // before the first query, none past N) run unmasked, in pairs so that the
@@ -251,15 +338,16 @@ struct DqKernel {
   }
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DELTA>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(DqParams p) {
-  __shared__ __attribute__((aligned(1024))) char s0[2 * DqKernel<D, CAUSAL>::TILE];
-  __shared__ __attribute__((aligned(1024))) char s1[2 * DqKernel<D, CAUSAL>::TILE];
-  DqKernel<D, CAUSAL> k(p, s0, s1);
+  using Kt = DqKernel<D, CAUSAL, DELTA>;
+  __shared__ __attribute__((aligned(1024))) char s0[2 * Kt::TILE];
+  __shared__ __attribute__((aligned(1024))) char s1[2 * Kt::TILE];
+  Kt k(p, s0, s1);
   k.run();
 }
 
-template <int D>
+template <int D, bool DELTA>
 hipError_t dq_d(const BwdArgs& a, hipStream_t stream) {
   DqParams p;
   p.q = static_cast<const uint16_t*>(a.q);
@@ -273,16 +361,24 @@ hipError_t dq_d(const BwdArgs& a, hipStream_t stream) {
   p.N = a.N;
   p.n_qblocks = (a.N + 127) / 128;
   p.scale = a.scale;
+  p.o = a.o;
+  p.dout_in = a.dout;
+  p.dout16 = a.dout16;
+  p.f32io = a.mode == kFp32Out ? 1 : 0;
   const unsigned grid = (unsigned)(p.BH * p.n_qblocks);
-  if (a.causal) hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3(grid), dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3(grid), dim3(256), 0, stream, p);
+  if (a.causal) hipLaunchKernelGGL((bwd_dq_kernel<D, true, DELTA>), dim3(grid), dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL((bwd_dq_kernel<D, false, DELTA>), dim3(grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
-  return a.d == 64 ? dq_d<64>(a, stream) : dq_d<128>(a, stream);
+  return a.d == 64 ? dq_d<64, false>(a, stream) : dq_d<128, false>(a, stream);
+}
+
+hipError_t launch_bwd_dq_delta(const BwdArgs& a, hipStream_t stream) {
+  return a.d == 64 ? dq_d<64, true>(a, stream) : dq_d<128, true>(a, stream);
 }
 
 }  // namespace pfa

@@ -67,11 +67,15 @@ constexpr size_t kNoallocScratchBytes = size_t(72) << 20;
 int noalloc_scratch(void* stream, void** ptr);
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
-// The backward in three kernels on one stream: delta = rowsum(dO o O); dK and
-// dV; dQ.
+// The backward's kernels on one stream: delta = rowsum(dO o O); dK and dV;
+// dQ.
 hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
+// dQ that also forms delta = rowsum(dO o O) (bit for bit the pre-pass's) and,
+// in the FP32-output mode, the BF16 copy of dO: it replaces the pre-pass when
+// it runs before the dK/dV kernel.
+hipError_t launch_bwd_dq_delta(const BwdArgs& a, hipStream_t stream);
 // delta from another source (kDeltaDpP, kDeltaOhp) or delta_lp - delta_hp
 // (kDeltaErr), written to `out` [B,H,N].
 hipError_t launch_bwd_delta(const BwdArgs& a, int src, float* out, hipStream_t stream);

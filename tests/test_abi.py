@@ -146,6 +146,16 @@ def test_backward_stages_reject_invalid_arguments(L):
     bad = list(dq_args)
     bad[12] = 48
     assert L.attn_bwd_dq(*bad) == uns
+    # attn_bwd_dq_delta: the dQ arguments plus o
+    dd_args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, need, 1, 1, 128, 64, 1, 0.125, 0, None]
+    for pos, val in ((3, None), (3, FAKE + 2), (5, None), (6, FAKE + 4), (7, FAKE + 1), (9, need - 1),
+                     (15, float("inf")), (16, 4)):
+        bad = list(dd_args)
+        bad[pos] = val
+        assert L.attn_bwd_dq_delta(*bad) == inv, pos
+    bad = list(dd_args)
+    bad[13] = 96
+    assert L.attn_bwd_dq_delta(*bad) == uns
 
 
 def test_delta_entry_points_reject_invalid_arguments(L):

@@ -494,27 +494,43 @@ def test_ragged_large_shapes(gpu, name, wl, slices, mode, causal):
         assert gf.sum() > 0
 
 
+STAGE_SHAPES = [
+    ("b2_h2_n260_d128", Workload(89, "stages", 2, 2, 260, 128, tie_frac=0.05, tie_q_scale=8.0), True),
+    ("b1_h3_n333_d64", Workload(88, "stages64", 1, 3, 333, 64, tie_frac=0.05, tie_q_scale=8.0), True),
+    ("noncausal_b4_h8_n97_d128", Workload(87, "stages_nc", 4, 8, 97, 128, tie_frac=0.05), False),
+]
+
+
 @pytest.mark.parametrize("mode", MODES)
-def test_backward_stages_equal_one_call(gpu, mode):
-    """attn_bwd_prep + attn_bwd_dkdv + attn_bwd_dq on one stream give bit for
-    bit what attn_bwd gives (no atomics anywhere)."""
+@pytest.mark.parametrize("name,wl,causal", STAGE_SHAPES, ids=[c[0] for c in STAGE_SHAPES])
+def test_backward_stages_equal_one_call(gpu, name, wl, causal, mode):
+    """attn_bwd_prep + attn_bwd_dkdv + attn_bwd_dq, and attn_bwd_dq_delta +
+    attn_bwd_dkdv, on one stream give bit for bit what attn_bwd gives (no
+    atomics anywhere), delta included: the dQ kernel that forms delta sums it
+    in the pre-pass's order."""
     import precision_flash_attention_attn_amd as pfa
-    wl = Workload(89, "stages", 2, 2, 260, 128, tie_frac=0.05, tie_q_scale=8.0)
+    print(f"[stages] {name} mode={mode}", flush=True)
     inp = generate(wl)
     q, k, v = (gpu.dev_bf16(x) for x in (inp.q, inp.k, inp.v))
     do = gpu.dev_f32(inp.do_f32) if mode == "fp32_out" else gpu.dev_bf16(inp.do_bf16)
-    o, lse, _ = pfa.forward(q, k, v, mode=mode)
-    dq1, dk1, dv1, de1 = pfa.backward(q, k, v, o, do, lse, mode=mode, want_delta=True)
-    ws = torch.full((pfa.attn_bwd_workspace_bytes(*q.shape, mode),), 0x7F, device=q.device,
-                    dtype=torch.uint8)  # garbage on entry
-    dq2, dk2, dv2 = (torch.empty_like(q) for _ in range(3))
-    pfa.attn_bwd_prep(o, do, ws, mode=mode)
-    pfa.attn_bwd_dkdv(q, k, v, do, lse, dk2, dv2, ws, mode=mode)
-    pfa.attn_bwd_dq(q, k, v, do, lse, dq2, ws, mode=mode)
-    torch.cuda.synchronize()
+    o, lse, _ = pfa.forward(q, k, v, causal=causal, mode=mode)
+    dq1, dk1, dv1, de1 = pfa.backward(q, k, v, o, do, lse, causal=causal, mode=mode, want_delta=True)
     h = gpu.host
-    for a, b in ((dq1, dq2), (dk1, dk2), (dv1, dv2)):
-        assert np.array_equal(h(a), h(b))
+    for two in (False, True):
+        ws = torch.full((pfa.attn_bwd_workspace_bytes(*q.shape, mode),), 0x7F, device=q.device,
+                        dtype=torch.uint8)  # garbage on entry
+        dq2, dk2, dv2 = (torch.full_like(q, 3.0) for _ in range(3))
+        de2 = torch.full_like(lse, 5.0)
+        if two:
+            pfa.attn_bwd_dq_delta(q, k, v, o, do, lse, dq2, ws, delta=de2, causal=causal, mode=mode)
+        else:
+            pfa.attn_bwd_prep(o, do, ws, delta=de2, mode=mode)
+        pfa.attn_bwd_dkdv(q, k, v, do, lse, dk2, dv2, ws, delta=de2, causal=causal, mode=mode)
+        if not two:
+            pfa.attn_bwd_dq(q, k, v, do, lse, dq2, ws, delta=de2, causal=causal, mode=mode)
+        torch.cuda.synchronize()
+        for a, b in ((dq1, dq2), (dk1, dk2), (dv1, dv2), (de1, de2)):
+            assert np.array_equal(h(a), h(b)), two
 
 
 LONG = [
