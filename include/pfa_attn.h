@@ -33,9 +33,10 @@
  * [B, H, N] for LSE, delta and tie flags.  Q, K, V, dQ, dK, dV are BF16; O and
  * dO are BF16 except in PFA_FP32_OUT, where they are FP32.  All pointers are
  * DEVICE pointers owned by the caller, 16-byte aligned.  The library allocates
- * no memory, keeps no state between calls and launches only on the given
- * stream (a hipStream_t; NULL is the default stream).  Calls are asynchronous:
- * a device fault surfaces at the caller's next synchronisation.
+ * no memory, keeps no state between calls (attn_bwd_noalloc's static scratch
+ * aside, see there) and launches only on the given stream (a hipStream_t;
+ * NULL is the default stream).  Calls are asynchronous: a device fault
+ * surfaces at the caller's next synchronisation.
  *
  * Supported: d in {64, 128}; any N >= 1 (ragged tails are masked) with
  * N*d < 2^29 (byte offsets inside one (batch, head) slice stay 32-bit);
