@@ -206,6 +206,15 @@ bool ok16(const void* p) { return p && aligned16(p); }
 
 int status_of(hipError_t e) { return e == hipSuccess ? PFA_OK : PFA_ERR_HIP; }
 
+// The backward with delta = rowsum(dO o O): the dQ kernel first, which also
+// forms delta (and the BF16 dO of the FP32-output mode) for the dK/dV kernel,
+// so no pre-pass over O and dO is needed.
+int bwd_standard(const pfa::BwdArgs& a, hipStream_t s) {
+  hipError_t e = pfa::launch_bwd_dq_delta(a, s);
+  if (e == hipSuccess) e = pfa::launch_bwd_dkdv(a, s);
+  return status_of(e);
+}
+
 }  // namespace
 
 int attn_bwd_prep(const void* o, const void* dout, float* delta, void* workspace,
@@ -294,12 +303,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  // dQ first: it also forms delta (and the BF16 dO of the FP32-output mode)
-  // for the dK/dV kernel, which saves the pre-pass over O and dO
-  hipError_t e = pfa::launch_bwd_dq_delta(a, s);
-  if (e == hipSuccess) e = pfa::launch_bwd_dkdv(a, s);
-  return status_of(e);
+  return bwd_standard(a, static_cast<hipStream_t>(stream));
 }
 
 int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -330,12 +334,7 @@ int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  // dQ first: it also forms delta (and the BF16 dO of the FP32-output mode)
-  // for the dK/dV kernel, which saves the pre-pass over O and dO
-  hipError_t e = pfa::launch_bwd_dq_delta(a, s);
-  if (e == hipSuccess) e = pfa::launch_bwd_dkdv(a, s);
-  return status_of(e);
+  return bwd_standard(a, static_cast<hipStream_t>(stream));
 }
 
 size_t attn_bwd_noalloc_max_bytes(void) { return pfa::kNoallocScratchBytes; }
@@ -393,11 +392,7 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, cons
   a.dv = dv;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
-  if (delta_src == PFA_DELTA_DO_O) {
-    e = pfa::launch_bwd_dq_delta(a, s);
-    if (e == hipSuccess) e = pfa::launch_bwd_dkdv(a, s);
-    return status_of(e);
-  }
+  if (delta_src == PFA_DELTA_DO_O) return bwd_standard(a, s);
   if (mode == PFA_FP32_OUT) e = pfa::launch_bwd_prep(a, s);
   if (e == hipSuccess) e = pfa::launch_bwd_delta(a, delta_src, a.delta, s);
   if (e == hipSuccess) e = pfa::launch_bwd_dkdv(a, s);
